@@ -1,0 +1,185 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MI355X (gfx950) fused MoE forward.
+ *
+ * The path (pages cited by title, sections as printed on each page):
+ *   [FMF8]  "Fused MoE FP8: 8.09 -> 13.18 TFLOPS (1.63x)" (Croqtile tutorial): pipeline
+ *           overview, problem table, "Baseline: 7 kernels" items 1-7, Phase 1 fusions.
+ *   [H200]  "H200 MoE Grouped GEMM: routed-row accounting, online replay and SM90 tuning":
+ *           compact routed rows, gated-up and down projections (BF16 grouped GEMM).
+ *   [WEAVE] repost blog on the "Weave" paper: persistent kernel pulling
+ *           (expert, token_begin, token_num) tasks from an atomic counter (sections 2.2, 4.2,
+ *           4.3).
+ *
+ *   route -> count + layout (+ task list) -> quantise + sort + gather -> grouped GEMM ->
+ *   routing-weighted combine to BF16.
+ *
+ * Conventions that hold for every entry point:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except where a comment
+ *     says "host".  The library never allocates, frees or synchronises inside these calls
+ *     (moe_forward's first call for a given shape builds and caches a graph, see there).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and is
+ *     asynchronous; calls made under stream capture are recorded like any other launch.
+ *   - Arrays are row-major, last index contiguous.  bf16 travels as uint16_t bit patterns;
+ *     FP8 is OCP E4M3FN (bias 7, max 448, 0x7F/0xFF NaN) as uint8_t.
+ *   - k (top-k) is at most 64 and at most E; E is at most 1024.
+ *   - Argument checks run on the host before any HIP call.  Return values: MOE_OK, or a
+ *     negative status; nothing is thrown across the ABI.  Invalid arguments launch nothing.
+ *   - topk_ids produced by moe_route are always in [0, E).  Ids supplied by a caller that lie
+ *     outside [0, E) are skipped by every later stage (that route contributes nothing).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_E_INVAL (-1)  /* bad sizes, null pointer, unsupported combination         */
+#define MOE_E_NOSPC (-2)  /* caller-provided buffer (tasks, workspace) is too small    */
+#define MOE_E_HIP (-3)    /* a HIP launch or runtime call failed                       */
+#define MOE_E_DEVICE (-4) /* no HIP device, or the current device is not gfx950        */
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* One unit of grouped-GEMM work ([WEAVE] section 4.2): rows [row_begin, row_begin+row_count)
+ * of expert `expert`'s segment, times the weight panel n_block (n_tile output columns). */
+typedef struct moe_task {
+    int32_t expert;
+    int32_t row_begin;
+    int32_t row_count;
+    int32_t n_block;
+} moe_task;
+
+/* Grouped GEMM operand types. */
+#define MOE_GEMM_FP8_B128 0 /* E4M3 operands, 1x128 activation / 128x128 weight fp32 scales */
+#define MOE_GEMM_BF16 1     /* bf16 operands, no scales                                     */
+
+/* Grouped GEMM epilogues (what is written for sorted row r, output column n). */
+#define MOE_EPI_STORE_F32 0   /* out f32 [rows][N]: out[r][n]                              */
+#define MOE_EPI_STORE_BF16 1  /* out bf16 [rows][N]: bf16(out[r][n]), round to nearest even */
+#define MOE_EPI_ROUTE_F32 2   /* out f32 [M*k][N]: out[sorted_route_ids[r]][n], i.e. each
+                                 routed row lands at its route id t*k+j for the combine   */
+#define MOE_EPI_SWIGLU_BF16 3 /* BF16 mode only; out bf16 [rows][N/2]:
+                                 bf16(silu(h[r][c]) * h[r][N/2+c]) for c < N/2             */
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* MOE_OK when the current HIP device is a gfx950; MOE_E_DEVICE otherwise. */
+int moe_device_check(void);
+
+/* ---- [FMF8] Baseline item 1 (Route): softmax with softcapping (tanh), then top-k --------
+ * logits f32 [M][E].  For each token: the k experts with the largest raw logit, ties to the
+ * lower index (-0 equals +0), written to topk_ids [M][k] in descending order; their weights
+ * topk_weights [M][k] = softmax over c_j = softcap*tanh(logit_j/softcap) of the k selected
+ * experts (renormalised to sum 1).  softcap <= 0 disables the cap (c = logit).  Logits must
+ * be finite. */
+int moe_route(const float* logits, int M, int E, int k, float softcap, int32_t* topk_ids,
+              float* topk_weights, moe_stream_t stream);
+
+/* ---- [FMF8] Baseline items 2-3 + Fusion 3 (count and build layout), [WEAVE] 4.3 ---------
+ * Host only (no HIP call): capacity that `tasks` needs for moe_build_layout, i.e.
+ * (floor(M*k/chunk_rows) + min(E, M*k)) * n_blocks.  Returns -1 on bad arguments. */
+int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows);
+
+/* topk_ids s32 [M][k] ->
+ *   counts s32 [E]       routes per expert
+ *   offsets s32 [E+1]    exclusive prefix sum; offsets[E] = number of valid routes (M*k)
+ *   cursors s32 [E]      = offsets[0..E-1]; moe_quant_sort_gather advances them
+ *   tasks [max_tasks]    each expert's rows cut into chunks of at most chunk_rows rows,
+ *                        each chunk crossed with n_blocks weight panels; full chunks first,
+ *                        then the partial ones by decreasing row count (largest first)
+ *   ntasks s32 [1]       number of tasks written
+ *   queue u32 [2]        reset to zero (the grouped GEMM's persistent work queue)
+ * chunk_rows in [1, 1024]; max_tasks must be >= moe_max_tasks(...) (else MOE_E_NOSPC).
+ * One workgroup of 1024 threads; the order of tasks with equal row counts is unspecified. */
+int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
+                     int chunk_rows, int32_t* counts, int32_t* offsets, int32_t* cursors,
+                     moe_task* tasks, int max_tasks, int32_t* ntasks, uint32_t* queue,
+                     moe_stream_t stream);
+
+/* ---- [FMF8] Baseline items 4-5 + Fusion 2 (QSG: quantise, sort, gather) ------------------
+ * x bf16 [M][K], K a multiple of 128.  Per token and 128-wide block b:
+ *   amax = max|x|, scale = amax/448 (fp32, correctly rounded), inv = 1/scale (fp32,
+ *   correctly rounded), code = E4M3(x*inv) rounded to nearest even, |y| >= 448 saturating to
+ *   0x7E|sign, zeros keeping their sign; an all-zero block gets scale 0 and sign-only codes.
+ * Each valid route r = t*k+j takes slot = atomicAdd(cursors[topk_ids[r]], 1) and writes
+ *   sorted_route_ids[slot] = r, a_q[slot][0..K) = codes of token t,
+ *   a_scales[b][slot] = scale of token t, block b   (a_scales is [K/128][M*k]).
+ * The order of routes inside one expert segment depends on atomic arrival order. */
+int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
+                          int E, int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
+                          float* a_scales, moe_stream_t stream);
+
+/* ---- [FMF8] problem table (128x128 blockwise weights): weight preparation ---------------
+ * w f32 [E][N][K] -> w_q E4M3 [E][N][K] and w_scales f32 [E][N/128][K/128], with the
+ * activation rule above applied to every 128x128 block.  N, K multiples of 128. */
+int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, float* w_scales,
+                         moe_stream_t stream);
+
+/* ---- [FMF8] Baseline item 6 (grouped GEMM) + [WEAVE] persistent atomic task queue -------
+ * Output column tile of one task, per operand mode: 128 for MOE_GEMM_FP8_B128. */
+int moe_gemm_n_tile(int mode);
+
+/* For every task (e, r0, nr, nb) in tasks[0..*ntasks) and every row r in [r0, r0+nr),
+ * column n in the task's panel [nb*n_tile, (nb+1)*n_tile):
+ *   FP8_B128:  h[r][n] = sum_b a_scales[b][r] * w_scales[e][n/128][b] *
+ *                        sum_{k in block b} e4m3(a[r][k]) * e4m3(w[e][n][k])   (fp32 accum)
+ *   BF16:      h[r][n] = sum_k a[r][k] * w[e][n][k]                           (fp32 accum)
+ * and the epilogue writes h (see MOE_EPI_*).  a is [rows][K] (u8 or bf16); w is [E][N][K].
+ * a_scales/w_scales are ignored in BF16 mode.  sorted_route_ids [rows] is read only by
+ * MOE_EPI_ROUTE_F32 (may be NULL otherwise).
+ * Scheduling: with queue != NULL, a persistent grid pulls task indices from queue[0] with
+ * atomics; the last workgroup to leave resets queue[0..1] to zero, so the call can be
+ * repeated or graph-replayed.  With queue == NULL, the same grid walks the task list with a
+ * fixed stride.  Tasks must come from moe_build_layout for the same rows, E, n_tile and
+ * chunk_rows (FP8_B128: chunk_rows <= 64).  The expert weights are streamed once per task,
+ * so every task of the same expert re-reads its panel (from HBM or the caches). */
+int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
+                     const void* w, const float* w_scales, int E, int N,
+                     const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                     int chunk_rows, uint32_t* queue, int epilogue,
+                     const int32_t* sorted_route_ids, void* out, moe_stream_t stream);
+
+/* ---- [FMF8] Baseline item 7 (scatter, routing-weighted) ---------------------------------
+ * route_rows f32 [M*k][N] holds the GEMM row of route t*k+j (MOE_EPI_ROUTE_F32).
+ *   out[t][n] = bf16( sum_{j: topk_ids[t][j] valid} topk_weights[t][j] * route_rows[t*k+j][n] )
+ * summed in fp32 in j order and rounded to nearest even once.  N a multiple of 4. */
+int moe_scatter(const float* route_rows, const float* topk_weights, const int32_t* topk_ids,
+                int M, int k, int E, int N, uint16_t* out, moe_stream_t stream);
+
+/* ---- whole step: route -> layout -> QSG -> FP8 grouped GEMM -> combine -------------------
+ * Workspace (device, caller-owned) of at least moe_forward_workspace_bytes(...) bytes. */
+size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
+
+/* Byte offset inside the workspace of one intermediate, for inspection in tests:
+ * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
+ * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 route_rows.  -1 on bad arguments. */
+int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
+
+/* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]
+ * -> out bf16 [M][N].  K, N multiples of 128.
+ * The five stages are enqueued on `stream` with no host synchronisation.  Unless the stream
+ * is being captured by the caller, the sequence is captured once into a HIP graph per
+ * (shape, softcap, pointers, options) and replayed on later calls. */
+int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* moe_forward with explicit options: chunk_rows (0 = chosen from M*k/E), flags bit 0 = no
+ * graph (plain launches), bit 1 = fixed-stride task walk instead of the atomic queue. */
+#define MOE_FWD_NO_GRAPH 1
+#define MOE_FWD_STATIC_GRID 2
+int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                   const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                   uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
+                   int flags, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,370 @@
+// api.hip -- the C ABI of libmoe.so (declared in include/moe.h): host-side argument checks,
+// the gfx950 device check, workspace carving and the graph-cached whole-step forward
+// ([FMF8] Phase 2: launches without host synchronisation, the serving path captured once as
+// a graph and replayed with a single launch; the output memset fused away).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+struct DevState {
+    int checked = 0;   // 0 unknown, 1 gfx950, -1 not usable
+    DeviceInfo info{0};
+    hipStream_t capture = nullptr;
+};
+DevState g_dev[kMaxDevices];
+std::mutex g_mu;
+thread_local int t_dev = 0;
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MOE_E_DEVICE;
+    }
+    t_dev = dev;
+    DevState& d = g_dev[dev];
+    if (d.checked == 0) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (d.checked == 0) {
+            hipDeviceProp_t p;
+            if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+                (void)hipGetLastError();
+                d.checked = -1;
+            } else {
+                d.info.cu_count = p.multiProcessorCount;
+                d.checked = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+            }
+        }
+    }
+    return d.checked == 1 ? MOE_OK : MOE_E_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+bool route_dims_ok(int M, int E, int k) {
+    return M >= 0 && E >= 1 && E <= kMaxE && k >= 1 && k <= E && k <= kMaxK &&
+           (long long)M * k <= INT_MAX && (long long)M * E <= (long long)INT_MAX * 16;
+}
+
+long long max_tasks_ll(int M, int k, int E, int n_blocks, int chunk_rows) {
+    const long long R = (long long)M * k;
+    const long long nonempty = R < E ? R : E;
+    return (R / chunk_rows + nonempty) * n_blocks;
+}
+
+// ---- workspace of moe_forward ----------------------------------------------------------
+struct WsLayout {
+    size_t off[12];
+    size_t total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int M, int E, int k, int K, int N) {
+    const size_t R = (size_t)M * k;
+    const int Nb = N / 128;
+    const size_t tasks = (size_t)max_tasks_ll(M, k, E, Nb, 1);  // any chunk_rows fits
+    const size_t sz[12] = {
+        R * 4,                      // 0 topk_ids
+        R * 4,                      // 1 topk_weights
+        (size_t)E * 4,              // 2 counts
+        (size_t)(E + 1) * 4,        // 3 offsets
+        (size_t)E * 4,              // 4 cursors
+        tasks * sizeof(moe_task),   // 5 tasks
+        4,                          // 6 ntasks
+        8,                          // 7 queue
+        R * 4,                      // 8 sorted_route_ids
+        R * (size_t)K,              // 9 a_q
+        (size_t)(K / 128) * R * 4,  // 10 a_scales
+        R * (size_t)N * 4,          // 11 route rows
+    };
+    WsLayout L;
+    size_t p = 0;
+    for (int i = 0; i < 12; ++i) {
+        L.off[i] = p;
+        p = align256(p + sz[i]);
+    }
+    L.total = p;
+    return L;
+}
+
+bool forward_dims_ok(int M, int E, int k, int K, int N) {
+    return M >= 1 && route_dims_ok(M, E, k) && K >= 128 && K % 128 == 0 && N >= 128 &&
+           N % 128 == 0 && (long long)M * k * (long long)K < (1LL << 40);
+}
+
+int default_chunk(int M, int k, int E) {
+    const long long avg = ((long long)M * k + E - 1) / E;
+    if (avg <= 16) return 16;
+    if (avg <= 48) return 32;
+    return 64;
+}
+
+// ---- the enqueued step -----------------------------------------------------------------
+struct FwdArgs {
+    const float* logits;
+    const uint16_t* x;
+    const uint8_t* w_q;
+    const float* w_scales;
+    int M, E, k, K, N;
+    float softcap;
+    uint16_t* out;
+    void* ws;
+    int chunk, flags;
+};
+
+hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
+    const WsLayout L = ws_layout(a.M, a.E, a.k, a.K, a.N);
+    char* base = static_cast<char*>(a.ws);
+    auto at = [&](int i) { return base + L.off[i]; };
+    int32_t* ids = reinterpret_cast<int32_t*>(at(0));
+    float* wts = reinterpret_cast<float*>(at(1));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(2));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(3));
+    int32_t* cursors = reinterpret_cast<int32_t*>(at(4));
+    moe_task* tasks = reinterpret_cast<moe_task*>(at(5));
+    int32_t* ntasks = reinterpret_cast<int32_t*>(at(6));
+    uint32_t* queue = reinterpret_cast<uint32_t*>(at(7));
+    int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
+    uint8_t* a_q = reinterpret_cast<uint8_t*>(at(9));
+    float* a_s = reinterpret_cast<float*>(at(10));
+    float* rows = reinterpret_cast<float*>(at(11));
+    const int Nb = a.N / 128;
+    const int max_tasks = (int)max_tasks_ll(a.M, a.k, a.E, Nb, a.chunk);
+    hipError_t e;
+    if ((e = launch_route(a.logits, a.M, a.E, a.k, a.softcap, ids, wts, s)) != hipSuccess) return e;
+    if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
+                           max_tasks, ntasks, queue, s)) != hipSuccess)
+        return e;
+    if ((e = launch_qsg(a.x, a.M, a.K, ids, a.k, a.E, cursors, sorted, a_q, a_s, s)) !=
+        hipSuccess)
+        return e;
+    uint32_t* q = (a.flags & MOE_FWD_STATIC_GRID) ? nullptr : queue;
+    if ((e = launch_gemm_fp8(a_q, a_s, a.M * a.k, a.K, a.w_q, a.w_scales, a.E, a.N, tasks,
+                             ntasks, max_tasks, a.chunk, q, MOE_EPI_ROUTE_F32, sorted, rows,
+                             s)) != hipSuccess)
+        return e;
+    return launch_scatter(rows, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+}
+
+// graph cache: one executable graph per (device, arguments)
+struct GraphEntry {
+    int dev;
+    FwdArgs args;
+    hipGraphExec_t exec;
+};
+std::vector<GraphEntry> g_graphs;
+constexpr size_t kMaxGraphs = 64;
+
+bool same_args(const FwdArgs& a, const FwdArgs& b) {
+    return a.logits == b.logits && a.x == b.x && a.w_q == b.w_q && a.w_scales == b.w_scales &&
+           a.M == b.M && a.E == b.E && a.k == b.k && a.K == b.K && a.N == b.N &&
+           std::memcmp(&a.softcap, &b.softcap, sizeof(float)) == 0 && a.out == b.out &&
+           a.ws == b.ws && a.chunk == b.chunk && a.flags == b.flags;
+}
+
+int forward_graph(const FwdArgs& a, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int dev = t_dev;
+    for (auto& g : g_graphs)
+        if (g.dev == dev && same_args(g.args, a)) return hip_status(hipGraphLaunch(g.exec, s));
+    DevState& d = g_dev[dev];
+    if (!d.capture) {
+        if (hipStreamCreateWithFlags(&d.capture, hipStreamNonBlocking) != hipSuccess) {
+            d.capture = nullptr;
+            return MOE_E_HIP;
+        }
+    }
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(d.capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
+        return MOE_E_HIP;
+    const hipError_t le = enqueue_forward(a, d.capture);
+    const hipError_t ce = hipStreamEndCapture(d.capture, &graph);
+    if (le != hipSuccess || ce != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        (void)hipGetLastError();
+        return MOE_E_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) return MOE_E_HIP;
+    if (g_graphs.size() >= kMaxGraphs) {
+        (void)hipGraphExecDestroy(g_graphs.front().exec);
+        g_graphs.erase(g_graphs.begin());
+    }
+    g_graphs.push_back(GraphEntry{dev, a, exec});
+    return hip_status(hipGraphLaunch(exec, s));
+}
+
+}  // namespace
+
+const DeviceInfo& device_info() { return g_dev[t_dev].info; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_E_INVAL: return "MOE_E_INVAL: invalid argument";
+        case MOE_E_NOSPC: return "MOE_E_NOSPC: buffer too small";
+        case MOE_E_HIP: return "MOE_E_HIP: HIP launch or runtime error";
+        case MOE_E_DEVICE: return "MOE_E_DEVICE: no gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+int moe_device_check(void) { return check_device(); }
+
+int moe_route(const float* logits, int M, int E, int k, float softcap, int32_t* topk_ids,
+              float* topk_weights, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k)) return MOE_E_INVAL;
+    if (M > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_route(logits, M, E, k, softcap, topk_ids, topk_weights,
+                                   (hipStream_t)stream));
+}
+
+int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows) {
+    if (!route_dims_ok(M, E, k) || n_blocks < 1 || chunk_rows < 1 || chunk_rows > 1024)
+        return -1;
+    const long long v = max_tasks_ll(M, k, E, n_blocks, chunk_rows);
+    return v > INT_MAX ? -1 : (int)v;
+}
+
+int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
+                     int chunk_rows, int32_t* counts, int32_t* offsets, int32_t* cursors,
+                     moe_task* tasks, int max_tasks, int32_t* ntasks, uint32_t* queue,
+                     moe_stream_t stream) {
+    const int need = moe_max_tasks(M, k, E, n_blocks, chunk_rows);
+    if (need < 0) return MOE_E_INVAL;
+    if ((M > 0 && !topk_ids) || !counts || !offsets || !cursors || !ntasks || !queue)
+        return MOE_E_INVAL;
+    if (need > 0 && !tasks) return MOE_E_INVAL;
+    if (max_tasks < need) return MOE_E_NOSPC;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_layout(topk_ids, M, k, E, n_blocks, chunk_rows, counts, offsets,
+                                    cursors, tasks, max_tasks, ntasks, queue,
+                                    (hipStream_t)stream));
+}
+
+int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
+                          int E, int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
+                          float* a_scales, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || K < 128 || K % 128) return MOE_E_INVAL;
+    if (M > 0 && (!x || !topk_ids || !cursors || !sorted_route_ids || !a_q || !a_scales))
+        return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_qsg(x, M, K, topk_ids, k, E, cursors, sorted_route_ids, a_q,
+                                 a_scales, (hipStream_t)stream));
+}
+
+int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, float* w_scales,
+                         moe_stream_t stream) {
+    if (E < 1 || N < 128 || K < 128 || N % 128 || K % 128 || !w || !w_q || !w_scales)
+        return MOE_E_INVAL;
+    if ((long long)E * (N / 128) * (K / 128) > INT_MAX) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_quantize_weights(w, E, N, K, w_q, w_scales, (hipStream_t)stream));
+}
+
+int moe_gemm_n_tile(int mode) { return mode == MOE_GEMM_FP8_B128 ? 128 : -1; }
+
+int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
+                     const void* w, const float* w_scales, int E, int N,
+                     const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                     int chunk_rows, uint32_t* queue, int epilogue,
+                     const int32_t* sorted_route_ids, void* out, moe_stream_t stream) {
+    if (mode != MOE_GEMM_FP8_B128) return MOE_E_INVAL;
+    if (rows < 0 || E < 1 || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
+        return MOE_E_INVAL;
+    if (chunk_rows < 1 || chunk_rows > 64) return MOE_E_INVAL;
+    if (epilogue != MOE_EPI_STORE_F32 && epilogue != MOE_EPI_STORE_BF16 &&
+        epilogue != MOE_EPI_ROUTE_F32)
+        return MOE_E_INVAL;
+    if (!w || !w_scales || !ntasks || !out || (max_tasks > 0 && !tasks)) return MOE_E_INVAL;
+    if (rows > 0 && (!a || !a_scales)) return MOE_E_INVAL;
+    if (epilogue == MOE_EPI_ROUTE_F32 && !sorted_route_ids) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_gemm_fp8(static_cast<const uint8_t*>(a), a_scales, rows, K,
+                                      static_cast<const uint8_t*>(w), w_scales, E, N, tasks,
+                                      ntasks, max_tasks, chunk_rows, queue, epilogue,
+                                      sorted_route_ids, out, (hipStream_t)stream));
+}
+
+int moe_scatter(const float* route_rows, const float* topk_weights, const int32_t* topk_ids,
+                int M, int k, int E, int N, uint16_t* out, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || N < 4 || N % 4) return MOE_E_INVAL;
+    if (M > 0 && (!route_rows || !topk_weights || !topk_ids || !out)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_scatter(route_rows, topk_weights, topk_ids, M, k, E, N, out,
+                                     (hipStream_t)stream));
+}
+
+size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N) {
+    if (!forward_dims_ok(M, E, k, K, N)) return 0;
+    return ws_layout(M, E, k, K, N).total;
+}
+
+int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which) {
+    if (!forward_dims_ok(M, E, k, K, N) || which < 0 || which >= 12) return -1;
+    return (int64_t)ws_layout(M, E, k, K, N).off[which];
+}
+
+int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                   const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                   uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
+                   int flags, moe_stream_t stream) {
+    if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
+    if (!logits || !x || !w_q || !w_scales || !out || !workspace) return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
+    if (flags & ~(MOE_FWD_NO_GRAPH | MOE_FWD_STATIC_GRID)) return MOE_E_INVAL;
+    if (workspace_bytes < ws_layout(M, E, k, K, N).total) return MOE_E_NOSPC;
+    int rc = check_device();
+    if (rc) return rc;
+    FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
+              chunk_rows ? chunk_rows : default_chunk(M, k, E), flags};
+    hipStream_t s = (hipStream_t)stream;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_E_HIP;
+    }
+    if ((flags & MOE_FWD_NO_GRAPH) || cs != hipStreamCaptureStatusNone)
+        return hip_status(enqueue_forward(a, s));
+    return forward_graph(a, s);
+}
+
+int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    return moe_forward_ex(logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
+                          workspace_bytes, 0, 0, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// layout.hip -- per-expert counts, exclusive prefix sum, write cursors and the grouped-GEMM
+// task list in one workgroup ([FMF8] "Baseline: 7 kernels" items 2-3, Fusion 3 count and
+// build layout, Phase 5 parallel prefix scan and pipelined topk_ids loads; [WEAVE] section
+// 4.3 task-list construction: histogram, prefix sum, per-expert chunks).
+//
+// 1024 threads: ids are loaded four per thread before the LDS histogram atomics; the scan is
+// a wave64 shuffle scan plus a cross-wave scan of the 16 wave totals.  Tasks: the full
+// chunk_rows-row chunks of every expert first (expert order), then each expert's partial
+// chunk placed by a counting sort on its row count, largest first; every chunk is crossed
+// with the n_blocks weight panels (consecutive entries share the chunk).  The persistent
+// queue counter is reset here so the captured step needs no memset node.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+// Exclusive block scan of one int per thread; returns the exclusive prefix and the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int inc = wave_inclusive_scan(v);
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < kWaves ? s_wsum[lane] : 0;
+        const int winc = wave_inclusive_scan(w);
+        if (lane < kWaves) s_wsum[lane] = winc - w;        // exclusive wave base
+        if (lane == kWaves - 1) s_wsum[kWaves] = winc;    // block total
+    }
+    __syncthreads();
+    const int excl = inc - v + s_wsum[wave];
+    total = s_wsum[kWaves];
+    __syncthreads();                                      // s_wsum may be reused
+    return excl;
+}
+
+__global__ __launch_bounds__(kThreads) void layout_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
+    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue) {
+    __shared__ int s_cnt[kThreads];
+    __shared__ int s_hist[kThreads];      // number of experts whose partial chunk has size s
+    __shared__ int s_wsum[kWaves + 1];
+    const int tid = threadIdx.x;
+
+    s_cnt[tid] = 0;
+    s_hist[tid] = 0;
+    __syncthreads();
+
+    for (int base = 0; base < R; base += 4 * kThreads) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = base + u * kThreads + tid;
+            v[u] = r < R ? ids[r] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if ((unsigned)v[u] < (unsigned)E) atomicAdd(&s_cnt[v[u]], 1);
+    }
+    __syncthreads();
+
+    const int c = tid < E ? s_cnt[tid] : 0;
+    const int full = c / chunk;
+    const int tail = c - full * chunk;
+    int total_rows, total_full;
+    const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
+    const int full0 = block_exclusive_scan(full, s_wsum, total_full);
+
+    if (tail > 0) atomicAdd(&s_hist[tail], 1);
+    __syncthreads();
+    // descending scan over partial-chunk sizes: thread i looks at size chunk-1-i
+    const int size = chunk - 1 - tid;
+    const int h = size >= 1 ? s_hist[size] : 0;
+    int total_tails;
+    const int larger = block_exclusive_scan(h, s_wsum, total_tails);
+    if (size >= 1) s_hist[size] = larger;                 // first position of size `size`
+    __syncthreads();
+
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = row0;
+        cursors[tid] = row0;
+        if (tid == E - 1) offsets[E] = row0 + c;
+        for (int i = 0; i < full; ++i) {
+            const int p = full0 + i;
+            for (int nb = 0; nb < n_blocks; ++nb)
+                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
+                    make_int4(tid, row0 + i * chunk, chunk, nb);
+        }
+        if (tail > 0) {
+            const int p = total_full + atomicAdd(&s_hist[tail], 1);
+            for (int nb = 0; nb < n_blocks; ++nb)
+                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
+                    make_int4(tid, row0 + full * chunk, tail, nb);
+        }
+    }
+    if (tid == 0) {
+        ntasks[0] = (total_full + total_tails) * n_blocks;
+        queue[0] = 0u;
+        queue[1] = 0u;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
+                         int32_t* counts, int32_t* offsets, int32_t* cursors, moe_task* tasks,
+                         int max_tasks, int32_t* ntasks, uint32_t* queue, hipStream_t s) {
+    (void)max_tasks;  // capacity checked on the host against moe_max_tasks
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
+                       chunk_rows, counts, offsets, cursors, tasks, ntasks, queue);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// moe_internal.h -- host-side launchers of the gfx950 kernels (arguments already checked by
+// the C ABI layer in api.hip).  Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Device facts the launchers size grids with (cached per device by api.hip).
+struct DeviceInfo {
+    int cu_count;
+};
+const DeviceInfo& device_info();
+
+hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
+                        int32_t* ids, float* weights, hipStream_t s);
+
+hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
+                         int32_t* counts, int32_t* offsets, int32_t* cursors, moe_task* tasks,
+                         int max_tasks, int32_t* ntasks, uint32_t* queue, hipStream_t s);
+
+hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
+                      int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
+                      float* a_scales, hipStream_t s);
+
+hipError_t launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q,
+                                   float* w_scales, hipStream_t s);
+
+hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, int K,
+                           const uint8_t* w, const float* w_scales, int E, int N,
+                           const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                           int chunk_rows, uint32_t* queue, int epilogue,
+                           const int32_t* sorted_route_ids, void* out, hipStream_t s);
+
+hipError_t launch_scatter(const float* rows, const float* weights, const int32_t* ids, int M,
+                          int k, int E, int N, uint16_t* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,177 @@
+"""Thin ctypes binding of libmoe.so (C ABI declared in include/moe.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.  Functions take
+torch tensors that live on the current HIP device (uint16 tensors carry bf16 bits, uint8
+tensors carry E4M3 codes) and enqueue on torch's current stream unless a stream is given.
+A missing library raises immediately; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_E_INVAL = -1
+MOE_E_NOSPC = -2
+MOE_E_HIP = -3
+MOE_E_DEVICE = -4
+
+MOE_GEMM_FP8_B128 = 0
+MOE_GEMM_BF16 = 1
+
+MOE_EPI_STORE_F32 = 0
+MOE_EPI_STORE_BF16 = 1
+MOE_EPI_ROUTE_F32 = 2
+MOE_EPI_SWIGLU_BF16 = 3
+
+MOE_FWD_NO_GRAPH = 1
+MOE_FWD_STATIC_GRID = 2
+
+# entry points and their C signatures (names identical to include/moe.h)
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_device_check": (_I, []),
+    "moe_route": (_I, [_P, _I, _I, _I, _F, _P, _P, _P]),
+    "moe_max_tasks": (_I, [_I, _I, _I, _I, _I]),
+    "moe_build_layout": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "moe_quant_sort_gather": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_gemm_n_tile": (_I, [_I]),
+    "moe_grouped_gemm": (_I, [_I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I,
+                              _P, _P, _P]),
+    "moe_scatter": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_forward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
+    "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _I, _P]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        msg = lib().moe_status_string(status).decode()
+        super().__init__(f"{name} failed: {msg} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by mixture_experts_layer_softcap_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_layer_softcap_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != MOE_OK:
+        raise MoeError(name, rc)
+    return rc
+
+
+def device_check() -> int:
+    return lib().moe_device_check()
+
+
+def route(logits, k: int, softcap: float, topk_ids, topk_weights, stream=None):
+    M, E = logits.shape
+    _call("moe_route", _ptr(logits), M, E, k, softcap, _ptr(topk_ids), _ptr(topk_weights),
+          _stream(stream))
+
+
+def max_tasks(M: int, k: int, E: int, n_blocks: int, chunk_rows: int) -> int:
+    v = lib().moe_max_tasks(M, k, E, n_blocks, chunk_rows)
+    if v < 0:
+        raise MoeError("moe_max_tasks", MOE_E_INVAL)
+    return v
+
+
+def build_layout(topk_ids, E: int, n_blocks: int, chunk_rows: int, counts, offsets, cursors,
+                 tasks, ntasks, queue, stream=None):
+    M, k = topk_ids.shape
+    _call("moe_build_layout", _ptr(topk_ids), M, k, E, n_blocks, chunk_rows, _ptr(counts),
+          _ptr(offsets), _ptr(cursors), _ptr(tasks), tasks.shape[0], _ptr(ntasks), _ptr(queue),
+          _stream(stream))
+
+
+def quant_sort_gather(x, topk_ids, E: int, cursors, sorted_route_ids, a_q, a_scales,
+                      stream=None):
+    M, K = x.shape
+    k = topk_ids.shape[1]
+    _call("moe_quant_sort_gather", _ptr(x), M, K, _ptr(topk_ids), k, E, _ptr(cursors),
+          _ptr(sorted_route_ids), _ptr(a_q), _ptr(a_scales), _stream(stream))
+
+
+def quantize_weights(w, w_q, w_scales, stream=None):
+    E, N, K = w.shape
+    _call("moe_quantize_weights", _ptr(w), E, N, K, _ptr(w_q), _ptr(w_scales), _stream(stream))
+
+
+def gemm_n_tile(mode: int) -> int:
+    return lib().moe_gemm_n_tile(mode)
+
+
+def grouped_gemm(mode: int, a, a_scales, w, w_scales, tasks, ntasks, chunk_rows: int, out,
+                 epilogue: int, queue=None, sorted_route_ids=None, stream=None):
+    rows, K = a.shape
+    E, N, _ = w.shape
+    _call("moe_grouped_gemm", mode, _ptr(a), _ptr(a_scales), rows, K, _ptr(w), _ptr(w_scales),
+          E, N, _ptr(tasks), _ptr(ntasks), tasks.shape[0], chunk_rows, _ptr(queue), epilogue,
+          _ptr(sorted_route_ids), _ptr(out), _stream(stream))
+
+
+def scatter(route_rows, topk_weights, topk_ids, E: int, out, stream=None):
+    M, k = topk_ids.shape
+    N = route_rows.shape[1]
+    _call("moe_scatter", _ptr(route_rows), _ptr(topk_weights), _ptr(topk_ids), M, k, E, N,
+          _ptr(out), _stream(stream))
+
+
+def forward_workspace_bytes(M: int, E: int, k: int, K: int, N: int) -> int:
+    v = lib().moe_forward_workspace_bytes(M, E, k, K, N)
+    if v == 0:
+        raise MoeError("moe_forward_workspace_bytes", MOE_E_INVAL)
+    return v
+
+
+def forward_workspace_offset(M: int, E: int, k: int, K: int, N: int, which: int) -> int:
+    return lib().moe_forward_workspace_offset(M, E, k, K, N, which)
+
+
+def forward(logits, x, w_q, w_scales, k: int, softcap: float, out, workspace,
+            chunk_rows: int = 0, flags: int = 0, stream=None):
+    M, E = logits.shape
+    K = x.shape[1]
+    N = w_q.shape[1]
+    _call("moe_forward_ex", _ptr(logits), _ptr(x), _ptr(w_q), _ptr(w_scales), M, E, k, K, N,
+          softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          chunk_rows, flags, _stream(stream))

@@ -1,0 +1,107 @@
+"""The C ABI on the host: libmoe.so loads, exports every entry point include/moe.h
+declares, and rejects bad arguments with status codes before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_softcap_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from mixture_experts_layer_softcap_amd import build
+
+        build.build()
+    return moe.lib()
+
+
+def test_every_declared_entry_point_is_exported(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(L):
+    assert L.moe_status_string(0) == b"MOE_OK"
+    for s in (-1, -2, -3, -4):
+        assert L.moe_status_string(s).startswith(b"MOE_E_")
+
+
+def test_max_tasks_bound(L):
+    # (floor(M*k/chunk) + min(E, M*k)) * n_blocks
+    assert L.moe_max_tasks(128, 8, 256, 4, 16) == (1024 // 16 + 256) * 4
+    assert L.moe_max_tasks(8, 2, 16, 2, 64) == (0 + 16) * 2
+    assert L.moe_max_tasks(1, 1, 256, 4, 16) == (0 + 1) * 4
+    assert L.moe_max_tasks(0, 8, 256, 4, 16) == 0
+    assert L.moe_max_tasks(128, 8, 256, 4, 0) == -1
+    assert L.moe_max_tasks(128, 9, 8, 4, 16) == -1      # k > E
+    assert L.moe_max_tasks(128, 65, 256, 4, 16) == -1   # k > 64
+    assert L.moe_max_tasks(128, 8, 2048, 4, 16) == -1   # E > 1024
+
+
+def test_workspace_queries(L):
+    b = L.moe_forward_workspace_bytes(128, 256, 8, 2048, 512)
+    R = 128 * 8
+    assert b >= R * 2048 + R * 512 * 4 + 16 * 4 * R
+    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(12)]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < b
+    assert L.moe_forward_workspace_bytes(128, 256, 8, 2000, 512) == 0   # K % 128
+    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 12) == -1
+
+
+NULL = None
+S = ctypes.c_void_p(0)
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def test_invalid_arguments_are_rejected_on_the_host(L):
+    INVAL, NOSPC = moe.MOE_E_INVAL, moe.MOE_E_NOSPC
+    assert L.moe_route(P, 4, 0, 1, 30.0, P, P, S) == INVAL            # E = 0
+    assert L.moe_route(P, 4, 8, 9, 30.0, P, P, S) == INVAL            # k > E
+    assert L.moe_route(NULL, 4, 8, 2, 30.0, P, P, S) == INVAL         # null logits
+    assert L.moe_route(P, 4, 8, 2, float("nan"), P, P, S) == INVAL    # NaN cap
+    assert L.moe_route(P, -1, 8, 2, 30.0, P, P, S) == INVAL
+    need = L.moe_max_tasks(16, 2, 8, 2, 4)
+    assert L.moe_build_layout(P, 16, 2, 8, 2, 4, P, P, P, P, need - 1, P, P, S) == NOSPC
+    assert L.moe_build_layout(P, 16, 2, 8, 2, 2000, P, P, P, P, 10 ** 6, P, P, S) == INVAL
+    assert L.moe_build_layout(P, 16, 2, 8, 2, 4, NULL, P, P, P, need, P, P, S) == INVAL
+    assert L.moe_quant_sort_gather(P, 4, 200, P, 2, 8, P, P, P, P, S) == INVAL   # K % 128
+    assert L.moe_quant_sort_gather(P, 4, 256, NULL, 2, 8, P, P, P, P, S) == INVAL
+    assert L.moe_quantize_weights(P, 2, 100, 256, P, P, S) == INVAL
+    assert L.moe_quantize_weights(NULL, 2, 128, 256, P, P, S) == INVAL
+    gg = L.moe_grouped_gemm
+    assert gg(7, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # mode
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 65, P, 0, P, P, S) == INVAL  # chunk
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 9, P, P, S) == INVAL  # epilogue
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 2, NULL, P, S) == INVAL  # route ids
+    assert gg(0, P, P, 4, 250, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # K % 128
+    assert L.moe_scatter(P, P, P, 4, 2, 8, 6, P, S) == INVAL          # N % 4
+    ws = L.moe_forward_workspace_bytes(8, 16, 2, 256, 256)
+    f = L.moe_forward_ex
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 4, S) == INVAL     # flags
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 65, 0, S) == INVAL    # chunk
+    assert f(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 0, S) == INVAL
+    assert L.moe_forward(P, P, P, P, 0, 16, 2, 256, 256, 30.0, P, P, ws, S) == INVAL
+
+
+def test_no_gpu_gives_a_device_status():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert moe.lib().moe_device_check() == moe.MOE_E_DEVICE

@@ -1,0 +1,426 @@
+"""GPU parity of every stage and of the whole forward against the CPU oracle.
+
+Integer results (ids, counts, offsets, task sets, segment contents, E4M3 codes, scales) are
+compared bit for bit; routing weights to 1e-5 relative; BF16 outputs with the relative
+Frobenius <= 5e-3 and per-element <= 2e-2*rms rule.  Rows inside one expert segment come in
+atomic arrival order on the GPU, so segments are sorted by route id before comparing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mixture_experts_layer_softcap_amd import moe, synth
+
+from gpu_util import (DEV, WEIGHT_RTOL, assert_bf16_close, canonical_segments, to_dev, to_np,
+                      workload, zeros)
+
+pytestmark = pytest.mark.gpu
+
+CAP = 30.0
+TINY = "fused_fp8_M8_E16_k2_K256_N256"
+QWEN = "fused_fp8_M128_E256_k8_K2048_N512"
+ZIPF1K = "fused_fp8_M1024_E256_k8_K2048_N512_zipf"
+ZIPF4K = "fused_fp8_M4096_E256_k8_K2048_N512_zipf"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc.build(force=False)
+    assert moe.device_check() == moe.MOE_OK, "current device is not gfx950"
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---- stage 1: route --------------------------------------------------------------------
+
+def gpu_route(logits, k, cap=CAP):
+    M, E = logits.shape
+    ids, w = zeros((M, k), torch.int32), zeros((M, k), torch.float32)
+    moe.route(to_dev(logits), k, cap, ids, w)
+    sync()
+    return to_np(ids), to_np(w)
+
+
+def check_route(logits, k, cap=CAP):
+    ids, w = gpu_route(logits, k, cap)
+    rids, rw = orc.route(logits, k, cap)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=WEIGHT_RTOL, atol=0)
+
+
+@pytest.mark.parametrize("name", [TINY, QWEN, ZIPF1K, ZIPF4K])
+def test_route_workloads(name):
+    d = synth.workload_inputs(name, weights=False)
+    check_route(d["logits"], d["k"])
+
+
+@pytest.mark.parametrize("M,E,k", [(1, 16, 1), (5, 16, 16), (33, 64, 8), (7, 1024, 8),
+                                   (9, 100, 3), (3, 1000, 64), (130, 256, 8)])
+def test_route_shapes(M, E, k):
+    g = np.random.default_rng(M * 7 + E + k)
+    logits = g.standard_normal((M, E)).astype(np.float32)
+    logits[:, ::3] = np.round(logits[:, ::3], 1)        # exact ties
+    check_route(logits, k)
+    check_route(logits, k, cap=0.0)
+
+
+def test_route_ties_and_signed_zero():
+    logits = np.zeros((4, 64), np.float32)
+    logits[1, [5, 9, 40]] = 1.0
+    logits[2, 7] = -0.0
+    logits[3] = -1.0
+    logits[3, [63, 0]] = -0.0
+    check_route(logits, 3)
+    ids, w = gpu_route(np.full((2, 16), 0.5, np.float32), 8)
+    assert (ids == np.arange(8)).all() and (w == np.float32(0.125)).all()
+
+
+# ---- stage 2: layout -------------------------------------------------------------------
+
+def gpu_layout(ids, E, n_blocks, chunk):
+    M, k = ids.shape
+    mt = moe.max_tasks(M, k, E, n_blocks, chunk)
+    counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
+    tasks = torch.full((max(mt, 1), 4), -7, dtype=torch.int32, device=DEV)
+    ntasks, queue = zeros(1, torch.int32), torch.full((2,), 5, dtype=torch.int32, device=DEV)
+    moe.build_layout(to_dev(ids), E, n_blocks, chunk, counts, offsets, cursors, tasks, ntasks,
+                     queue)
+    sync()
+    n = int(to_np(ntasks)[0])
+    return dict(counts=to_np(counts), offsets=to_np(offsets), cursors=to_np(cursors),
+                tasks=to_np(tasks)[:n], queue=to_np(queue), max_tasks=mt)
+
+
+def check_layout(ids, E, n_blocks, chunk):
+    g = gpu_layout(ids, E, n_blocks, chunk)
+    counts, offsets = orc.layout(ids, E)
+    np.testing.assert_array_equal(g["counts"], counts)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    np.testing.assert_array_equal(g["cursors"], offsets[:-1])
+    assert (g["queue"] == 0).all()
+    ref = orc.tasks(counts, offsets, n_blocks, chunk)
+    key = lambda t: sorted(map(tuple, t.tolist()))
+    assert key(g["tasks"]) == key(ref)
+    assert len(g["tasks"]) <= g["max_tasks"]
+    # order: every n_block of one chunk adjacent; full chunks first, then partial chunks by
+    # non-increasing row count
+    t = g["tasks"]
+    if len(t):
+        chunks = t.reshape(-1, n_blocks, 4)
+        assert (chunks[:, :, 3] == np.arange(n_blocks)).all()
+        assert (chunks[:, :, :3] == chunks[:, :1, :3]).all()
+        rc = chunks[:, 0, 2]
+        assert (np.diff(rc) <= 0).all()
+    return g
+
+
+@pytest.mark.parametrize("name,chunk", [(TINY, 16), (QWEN, 16), (ZIPF1K, 32), (ZIPF4K, 64),
+                                        (ZIPF4K, 1), (QWEN, 1024)])
+def test_layout_workloads(name, chunk):
+    d = synth.workload_inputs(name, weights=False)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    check_layout(ids, d["E"], d["N"] // 128, chunk)
+
+
+def test_layout_edge_cases():
+    # every route on one expert; empty experts; a single token; E = 1024
+    check_layout(np.full((40, 1), 3, np.int32), 8, 2, 16)
+    check_layout(np.array([[0]], np.int32), 1, 1, 1)
+    g = np.random.default_rng(3)
+    check_layout(g.integers(0, 1024, (300, 8)).astype(np.int32), 1024, 4, 7)
+    check_layout(g.integers(0, 5, (64, 2)).astype(np.int32), 300, 1, 16)
+
+
+# ---- stage 3: quantise + sort + gather -------------------------------------------------
+
+def gpu_qsg(x, ids, E, K):
+    M, k = ids.shape
+    lay = gpu_layout(ids, E, 1, 16)
+    cursors = to_dev(lay["offsets"][:-1].copy())
+    R = M * k
+    sorted_ids = torch.full((R,), -1, dtype=torch.int32, device=DEV)
+    a_q = zeros((R, K), torch.uint8)
+    a_s = zeros((K // 128, R), torch.float32)
+    moe.quant_sort_gather(to_dev(x), to_dev(ids), E, cursors, sorted_ids, a_q, a_s)
+    sync()
+    return to_np(sorted_ids), to_np(a_q), to_np(a_s), to_np(cursors), lay
+
+
+def check_qsg(x, ids, E):
+    K = x.shape[1]
+    s_ids, a_q, a_s, cursors, lay = gpu_qsg(x, ids, E, K)
+    counts, offsets = orc.layout(ids, E)
+    np.testing.assert_array_equal(cursors, offsets[1:])
+    q, s = orc.quant_act(x)
+    r_ids, r_aq, r_as = orc.sort_gather(ids, offsets, q, s)
+    perm = canonical_segments(s_ids, offsets)
+    np.testing.assert_array_equal(s_ids[perm], r_ids)
+    np.testing.assert_array_equal(a_q[perm], r_aq)
+    np.testing.assert_array_equal(a_s[:, perm].view(np.uint32), r_as.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", [TINY, QWEN, ZIPF1K])
+def test_qsg_workloads(name):
+    d = synth.workload_inputs(name, weights=False)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    check_qsg(d["x"], ids, d["E"])
+
+
+def test_qsg_edge_values():
+    # zero blocks, signed zeros, blocks whose amax is a power of two, tiny and huge values,
+    # odd K (3 blocks), K larger than one 2048-wide pass
+    g = np.random.default_rng(12)
+    for K in (384, 4096 + 128):
+        x = g.standard_normal((6, K)).astype(np.float32)
+        x[0, :128] = 0.0
+        x[0, 5] = -0.0
+        x[1, :128] *= np.float32(2.0 ** -60)
+        x[2, 128:256] = np.float32(448.0) * np.sign(x[2, 128:256])
+        x[3] *= np.float32(2.0 ** 40)
+        x[4, :] = np.float32(1.0)
+        xb = synth.bf16_bits(x)
+        ids = g.integers(0, 5, (6, 3)).astype(np.int32)
+        check_qsg(xb, ids, 5)
+
+
+# ---- weight preparation ------------------------------------------------------------------
+
+def gpu_wquant(w):
+    E, N, K = w.shape
+    w_q = zeros((E, N, K), torch.uint8)
+    w_s = zeros((E, N // 128, K // 128), torch.float32)
+    moe.quantize_weights(to_dev(w), w_q, w_s)
+    sync()
+    return to_np(w_q), to_np(w_s)
+
+
+def test_quantize_weights_full_qwen_layer():
+    d = workload(QWEN)
+    w_q, w_s = gpu_wquant(d["w"])
+    np.testing.assert_array_equal(w_s.view(np.uint32), d["w_s"].view(np.uint32))
+    np.testing.assert_array_equal(w_q, d["w_q"])
+
+
+def test_e4m3_encoder_sweep():
+    # blocks whose amax is exactly 448 have scale 1 and multiplier 1, so their codes are the
+    # plain encoding of the values: sweep fp32 bit patterns densely over [0, 448] and around
+    # every code value and midpoint
+    codes = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8)
+    table = np.unique(codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()).astype(np.float32)
+    mids = ((table[1:].astype(np.float64) + table[:-1]) / 2).astype(np.float32)
+    base = np.concatenate([table, mids]).view(np.uint32).astype(np.int64)
+    near = (base[:, None] + np.arange(-300, 301)[None, :]).ravel()
+    stride = np.arange(0, 0x43E00000, 97, dtype=np.int64)
+    bits = np.concatenate([near, stride])
+    bits = bits[(bits >= 0) & (bits <= 0x43E00000)].astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = np.concatenate([vals, -vals])
+    per_block = 128 * 128 - 1
+    nblk = -(-vals.size // per_block)
+    buf = np.zeros(nblk * per_block, np.float32)
+    buf[:vals.size] = vals
+    blocks = np.concatenate([np.full((nblk, 1), 448.0, np.float32),
+                             buf.reshape(nblk, per_block)], axis=1)
+    w = blocks.reshape(nblk, 128, 128)
+    w_q, w_s = gpu_wquant(w)
+    assert (w_s == 1.0).all()
+    r_q, r_s = orc.quant_weights(w)
+    np.testing.assert_array_equal(w_q, r_q)
+
+
+# ---- stage 4: grouped GEMM ---------------------------------------------------------------
+
+INT_CODES = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, -1: 0xB8, -2: 0xC0, -3: 0xC4,
+             -4: 0xC8}
+
+
+def int_codes(a):
+    out = np.zeros(a.shape, np.uint8)
+    for v, c in INT_CODES.items():
+        out[a == v] = c
+    return out
+
+
+def gpu_gemm(a_q, a_s, w_q, w_s, offsets, chunk, epilogue, sorted_ids=None, queue=True,
+             out_rows=None, repeat=1):
+    rows, K = a_q.shape
+    E, N, _ = w_q.shape
+    counts = np.diff(offsets).astype(np.int32)
+    tasks = orc.tasks(counts, offsets, N // 128, chunk)
+    tasks_d = to_dev(tasks if len(tasks) else np.zeros((1, 4), np.int32))
+    ntasks = to_dev(np.array([len(tasks)], np.int32))
+    q = zeros(2, torch.int32) if queue else None
+    n_out = rows if out_rows is None else out_rows
+    dt = torch.int16 if epilogue == moe.MOE_EPI_STORE_BF16 else torch.float32
+    out = torch.full((n_out, N), -3, dtype=dt, device=DEV)
+    args = (to_dev(a_q), to_dev(a_s), to_dev(w_q), to_dev(w_s))
+    sid = None if sorted_ids is None else to_dev(sorted_ids)
+    for _ in range(repeat):
+        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, *args, tasks_d, ntasks, chunk, out, epilogue,
+                         queue=q, sorted_route_ids=sid)
+    sync()
+    if q is not None:
+        assert (to_np(q) == 0).all(), "queue not reset by the last workgroup"
+    return to_np(out)
+
+
+@pytest.mark.parametrize("chunk,queue", [(16, True), (16, False), (32, True), (64, True),
+                                         (5, True)])
+def test_gemm_integer_exact(chunk, queue):
+    g = np.random.default_rng(chunk)
+    E, N, K = 4, 256, 512
+    counts = np.array([3, 0, 37, 70], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    Ai = g.integers(-4, 5, (rows, K))
+    Wi = g.integers(-4, 5, (E, N, K))
+    # power-of-two scales in [1/2, 2]: every partial sum stays an integer multiple of 2^-2
+    # below 2^15, so fp32 accumulation is exact in any order
+    sa = np.exp2(g.integers(-1, 2, (K // 128, rows))).astype(np.float32)
+    sb = np.exp2(g.integers(-1, 2, (E, N // 128, K // 128))).astype(np.float32)
+    ref = orc.gemm_fp8(int_codes(Ai), sa, int_codes(Wi), sb, offsets)
+    got = gpu_gemm(int_codes(Ai), sa, int_codes(Wi), sb, offsets, chunk,
+                   moe.MOE_EPI_STORE_F32, queue=queue, repeat=2)
+    np.testing.assert_array_equal(got, ref.astype(np.float32))
+
+
+def test_gemm_random_store_modes():
+    d = workload(TINY)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    counts, offsets = orc.layout(ids, d["E"])
+    q, s = orc.quant_act(d["x"])
+    sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
+    C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
+    rms = np.sqrt(np.mean(C ** 2))
+    f32 = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, 16, moe.MOE_EPI_STORE_F32)
+    assert np.abs(f32 - C).max() <= 1e-5 * rms
+    b16 = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, 16, moe.MOE_EPI_STORE_BF16)
+    assert_bf16_close(b16.view(np.uint16), C, "store bf16")
+    R = ids.size
+    rt = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, 16, moe.MOE_EPI_ROUTE_F32,
+                  sorted_ids=sorted_ids, out_rows=R)
+    np.testing.assert_array_equal(rt[sorted_ids], f32)
+
+
+def test_gemm_qwen_layer_rows():
+    d = workload(QWEN)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    counts, offsets = orc.layout(ids, d["E"])
+    q, s = orc.quant_act(d["x"])
+    sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
+    C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
+    rms = np.sqrt(np.mean(C ** 2))
+    for chunk, queue in ((16, True), (16, False)):
+        got = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, chunk, moe.MOE_EPI_STORE_F32,
+                       queue=queue)
+        assert np.abs(got - C).max() <= 1e-5 * rms, (chunk, queue)
+
+
+# ---- stage 5: scatter --------------------------------------------------------------------
+
+def test_scatter_matches_oracle():
+    g = np.random.default_rng(8)
+    M, k, E, N = 37, 8, 64, 384
+    ids = np.stack([g.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+    w = g.random((M, k)).astype(np.float32)
+    rows = g.standard_normal((M * k, N)).astype(np.float32)
+    out = zeros((M, N), torch.int16)
+    moe.scatter(to_dev(rows), to_dev(w), to_dev(ids), E, out)
+    sync()
+    y, y64 = orc.scatter(rows.astype(np.float64), np.arange(M * k, dtype=np.int32), w, M)
+    got = to_np(out).view(np.uint16)
+    assert_bf16_close(got, y64, "scatter")
+    # fp32 sum of 8 terms, then one rounding: at most one bf16 ulp from the exact rounding
+    diff = np.abs(got.astype(np.int32) - y.astype(np.int32))
+    assert diff.max() <= 1
+
+
+# ---- whole forward -----------------------------------------------------------------------
+
+def gpu_forward(d, flags=0, chunk=0, reps=1, keep_ws=False):
+    M, E, k, K, N = d["M"], d["E"], d["k"], d["K"], d["N"]
+    ws = zeros(moe.forward_workspace_bytes(M, E, k, K, N), torch.uint8)
+    out = zeros((M, N), torch.int16)
+    args = [to_dev(d["logits"]), to_dev(d["x"]), to_dev(d["w_q"]), to_dev(d["w_s"])]
+    outs = []
+    for _ in range(reps):
+        out.fill_(0)
+        moe.forward(*args, k, CAP, out, ws, chunk_rows=chunk, flags=flags)
+        sync()
+        outs.append(to_np(out).view(np.uint16).copy())
+    return (outs, ws) if keep_ws else outs
+
+
+def ws_part(ws, d, which, dtype, count):
+    off = moe.forward_workspace_offset(d["M"], d["E"], d["k"], d["K"], d["N"], which)
+    nbytes = count * np.dtype(dtype).itemsize
+    return to_np(ws[off:off + nbytes]).view(dtype)
+
+
+@pytest.mark.parametrize("flags", [0, moe.MOE_FWD_NO_GRAPH, moe.MOE_FWD_STATIC_GRID])
+@pytest.mark.parametrize("name", [TINY, QWEN])
+def test_forward_full(name, flags):
+    d = workload(name)
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], d["k"], CAP,
+                      intermediates=True)
+    (outs, ws) = gpu_forward(d, flags=flags, reps=3, keep_ws=True)
+    for y in outs:
+        assert_bf16_close(y, ref["y64"], f"{name} flags={flags}")
+        np.testing.assert_array_equal(y, outs[0])     # replays are bit-identical
+    R = d["M"] * d["k"]
+    np.testing.assert_array_equal(ws_part(ws, d, 0, np.int32, R).reshape(d["M"], d["k"]),
+                                  ref["ids"])
+    np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, d["E"]), ref["counts"])
+    np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, d["E"] + 1), ref["offsets"])
+
+
+@pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
+def test_forward_skewed_sampled(name):
+    d = workload(name)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    counts, _ = orc.layout(ids, d["E"])
+    assert counts.min() >= 1 and counts.max() / counts.min() >= 10
+    outs = gpu_forward(d, reps=2)
+    # sampled tokens: first, last, a seeded spread, and tokens routed to the busiest expert
+    busiest = int(np.argmax(counts))
+    on_busy = np.nonzero((ids == busiest).any(1))[0]
+    g = np.random.default_rng(0)
+    toks = np.unique(np.concatenate([[0, d["M"] - 1], g.choice(d["M"], 24, replace=False),
+                                     on_busy[:4], on_busy[-4:]])).astype(np.int32)
+    y, y64 = orc.forward_tokens(d["logits"], d["x"], d["w_q"], d["w_s"], d["k"], CAP, toks)
+    for o in outs:
+        assert_bf16_close(o[toks], y64, name)
+        np.testing.assert_array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("M,E,k,K,N,bias", [
+    (1, 16, 1, 128, 128, None),        # one token, one expert, smallest tiles
+    (3, 8, 8, 256, 256, None),         # k = E: every expert
+    (64, 8, 1, 384, 256, "one"),       # every route on one expert -> several chunks
+    (200, 300, 3, 128, 384, None),     # E not a multiple of 64, empty experts
+    (17, 64, 4, 2176, 128, None),      # K over one 2048 pass, ragged
+])
+def test_forward_edge_shapes(M, E, k, K, N, bias):
+    b = None
+    if bias == "one":
+        b = np.zeros(E, np.float32)
+        b[3] = 50.0
+    d = synth.fused_inputs(M, E, k, K, N, seed=M + E, bias=b)
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
+    for flags in (0, moe.MOE_FWD_STATIC_GRID):
+        y = gpu_forward(d, flags=flags)[0]
+        assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N}")
+
+
+def test_forward_repeat_determinism():
+    d = workload(QWEN)
+    outs = gpu_forward(d, reps=20)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
