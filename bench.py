@@ -1,0 +1,208 @@
+"""Benchmark of the fused FP8 MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole forward (route -> layout -> QSG -> FP8 grouped GEMM -> combine), replayed
+from the library's cached HIP graph, on the Qwen3.5-35B-A3B-shaped layer of the Fused MoE
+FP8 tutorial's problem table: M=128 tokens, 256 experts, top-8, K=2048, N=512.  Inputs are
+seeded synthetic data resident in HBM before timing; the weights are rotated over enough
+copies (>= 1 GiB) that every step streams them from HBM rather than from the 256 MB
+Infinity Cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+WEIGHT_BYTES_ROTATION = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="fused_fp8_M128_E256_k8_K2048_N512")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--static-grid", action="store_true",
+                   help="walk the task list with a fixed stride instead of the atomic queue")
+    p.add_argument("--chunk-rows", type=int, default=0)
+    return p.parse_args()
+
+
+def gemm_algorithmic_bytes(counts, M, k, K, N):
+    """Bytes the grouped GEMM must move: each non-empty expert's FP8 weights and scales once,
+    the routed FP8 rows and their scales once, the fp32 routed output rows once."""
+    nonempty = int((counts > 0).sum())
+    R = M * k
+    Nb, Kb = N // 128, K // 128
+    weights = nonempty * (N * K + Nb * Kb * 4)
+    acts = R * K + Kb * R * 4 + R * 4
+    out = R * N * 4
+    return weights + acts + out
+
+
+def layer_algorithmic_bytes(counts, M, E, k, K, N):
+    """Bytes the whole layer must move: used expert weights + scales, logits, x, output."""
+    nonempty = int((counts > 0).sum())
+    return nonempty * (N * K + (N // 128) * (K // 128) * 4) + M * E * 4 + M * K * 2 + M * N * 2
+
+
+def cpu_baseline(d, k, cap, budget_s=12.0):
+    import oracle
+
+    oracle.build(force=not os.path.exists(oracle.LIB_PATH))
+    w_q, w_s = oracle.quant_weights(d["w"])          # input preparation, not timed
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        oracle.forward(d["logits"], d["x"], w_q, w_s, k, cap)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": med * 1e6, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"whole layer ({d['M']} tokens, fp64 single-threaded C oracle), "
+                      f"median of {len(times)} runs; host has {os.cpu_count()} cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert-parallel path across GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_softcap_amd import moe, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rc = moe.device_check()
+    assert rc == moe.MOE_OK, f"not a gfx950 device ({rc})"
+
+    d = synth.workload_inputs(args.workload)
+    M, E, k, K, N, cap = d["M"], d["E"], d["k"], d["K"], d["N"], d["cap"]
+
+    # inputs resident in HBM; weights quantised on the GPU by the library
+    logits = torch.from_numpy(d["logits"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    w32 = torch.from_numpy(d["w"]).to(dev)
+    wq0 = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    ws0 = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    moe.quantize_weights(w32, wq0, ws0)
+    del w32
+    copies = max(1, -(-WEIGHT_BYTES_ROTATION // wq0.numel()))
+    wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+    wss = [ws0] + [ws0.clone() for _ in range(copies - 1)]
+    out = torch.empty((M, N), dtype=torch.int16, device=dev)
+    ws = torch.empty(moe.forward_workspace_bytes(M, E, k, K, N), dtype=torch.uint8, device=dev)
+    flags = moe.MOE_FWD_STATIC_GRID if args.static_grid else 0
+
+    def step(i):
+        moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
+                    chunk_rows=args.chunk_rows, flags=flags)
+
+    for i in range(max(args.warmup, copies)):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- whole-step timing: events around every graph replay ---------------------------
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]   # us
+    total_ms = evs[0].elapsed_time(evs[-1])
+    us_layer = total_ms * 1e3 / args.steps
+
+    # routing statistics of this input (read back from the workspace, outside timing)
+    off = moe.forward_workspace_offset(M, E, k, K, N, 2)
+    counts = ws[off:off + 4 * E].view(torch.int32).cpu().numpy()
+
+    # ---- dominant kernel alone: the grouped GEMM, same launch configuration ------------
+    def wsp(i, dtype, n):
+        o = moe.forward_workspace_offset(M, E, k, K, N, i)
+        return ws[o:o + n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+
+    R = M * k
+    chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (32 if -(-R // E) <= 48 else 64))
+    a_q = wsp(9, torch.uint8, R * K).view(R, K)
+    a_s = wsp(10, torch.float32, (K // 128) * R)
+    max_tasks = moe.max_tasks(M, k, E, N // 128, chunk)
+    tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
+    ntasks = wsp(6, torch.int32, 1)
+    queue = None if args.static_grid else wsp(7, torch.int32, 2)
+    sorted_ids = wsp(8, torch.int32, R)
+    rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
+    # the workspace still holds the layout of the last forward, built with the same chunk
+
+    def gemm(i):
+        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, wqs[i % copies], wss[i % copies],
+                         tasks, ntasks, chunk, rows_out, moe.MOE_EPI_ROUTE_F32, queue=queue,
+                         sorted_route_ids=sorted_ids)
+
+    for i in range(copies * 2):
+        gemm(i)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(args.steps):
+        gemm(i)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gemm_us = g0.elapsed_time(g1) * 1e3 / args.steps
+    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N)
+    achieved = gbytes / (gemm_us * 1e-6) / 1e9
+
+    lbytes = layer_algorithmic_bytes(counts, M, E, k, K, N)
+    flops = 2.0 * M * k * N * K
+    result = {
+        "metric": "µs/layer + effective TFLOPS & %HBM roofline, fused MoE M=128 E=256 top-8",
+        "value": round(us_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
+                   "softcap": cap, "weight_copies_rotated": copies,
+                   "task_walk": "static" if args.static_grid else "atomic queue",
+                   "chunk_rows": chunk},
+        "effective_tflops": round(flops / (us_layer * 1e-6) / 1e12, 3),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "layer_hbm_frac": round(lbytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_algorithmic_bytes": lbytes,
+        "nonempty_experts": int((counts > 0).sum()),
+        "roofline": {"bound": "hbm", "kernel": "gemm_fp8_kernel (grouped FP8 GEMM)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": gbytes,
+                     "avg_launch_us": round(gemm_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, k, cap)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -16,8 +16,6 @@ balanced / skewed expert-row distributions); and the Weave blog's Mixtral-like l
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 SOFTCAP = 30.0
@@ -73,10 +71,9 @@ def fused_inputs(M: int, E: int, k: int, K: int, N: int, seed: int = 0, bias=Non
     """Return dict(logits f32 [M,E], x bf16 bits [M,K], w f32 [E,N,K] or None)."""
     g = rng(seed)
     logits = g.standard_normal((M, E), dtype=np.float32)
-    if bias == "zipf":
-        logits = (logits + zipf_bias(E)[None, :]).astype(np.float32)
-    elif bias == "log":
-        logits = (logits + log_bias(E)[None, :]).astype(np.float32)
+    if isinstance(bias, str):
+        b = {"zipf": zipf_bias, "log": log_bias}[bias](E)
+        logits = (logits + b[None, :]).astype(np.float32)
     elif bias is not None:
         logits = (logits + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
     x = bf16_bits(g.standard_normal((M, K), dtype=np.float32))
@@ -152,13 +149,3 @@ def ffn_inputs(T: int, E: int, H: int, F: int, seed: int = 0, skewed: bool = Tru
     return dict(logits=logits, x=x, w_up=w_up, w_down=w_down)
 
 
-def fp8_flops(routed_rows: int, N: int, K: int) -> float:
-    """2 * (routed rows) * N * K, counted on compact routed rows."""
-    return 2.0 * routed_rows * N * K
-
-
-def ceil_div(a: int, b: int) -> int:
-    return -(-a // b)
-
-
-__all__ = [name for name in dir() if not name.startswith("_") and name not in ("math", "np")]

@@ -16,6 +16,12 @@ DEV = "cuda:0"
 REL_FRO = 5e-3
 ELEM_RMS = 2e-2
 WEIGHT_RTOL = 1e-5
+# fp32 rows of the FP8 grouped GEMM against the exact (double) oracle.  The matrix core sums
+# the 128 products of one scale block at reduced precision (about 2^-13 of the block's
+# magnitude was measured); the kernel promotes every block to fp32, so the error stays one
+# block's rounding per block.
+GEMM_F32_REL_FRO = 1e-4
+GEMM_F32_ELEM_RMS = 5e-4
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
@@ -51,6 +57,15 @@ def assert_bf16_close(y_bits: np.ndarray, ref64: np.ndarray, what: str = ""):
     worst = float(np.abs(y - ref).max()) if y.size else 0.0
     assert fro <= REL_FRO, f"{what}: relative Frobenius error {fro:.3e} > {REL_FRO}"
     assert worst <= ELEM_RMS * rms, f"{what}: max |d| {worst:.3e} > {ELEM_RMS}*rms ({rms:.3e})"
+
+
+def assert_gemm_f32_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    ref = np.asarray(ref, np.float64)
+    d = np.asarray(got, np.float64) - ref
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    fro = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    assert fro <= GEMM_F32_REL_FRO, f"{what}: relative Frobenius {fro:.3e}"
+    assert np.abs(d).max() <= GEMM_F32_ELEM_RMS * rms, f"{what}: max |d| {np.abs(d).max():.3e}"
 
 
 def canonical_segments(sorted_ids: np.ndarray, offsets: np.ndarray) -> np.ndarray:

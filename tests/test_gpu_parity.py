@@ -12,8 +12,8 @@ import torch
 import oracle as orc
 from mixture_experts_layer_softcap_amd import moe, synth
 
-from gpu_util import (DEV, WEIGHT_RTOL, assert_bf16_close, canonical_segments, to_dev, to_np,
-                      workload, zeros)
+from gpu_util import (DEV, WEIGHT_RTOL, assert_bf16_close, assert_gemm_f32_close,
+                      canonical_segments, to_dev, to_np, workload, zeros)
 
 pytestmark = pytest.mark.gpu
 
@@ -296,9 +296,8 @@ def test_gemm_random_store_modes():
     q, s = orc.quant_act(d["x"])
     sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
     C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
-    rms = np.sqrt(np.mean(C ** 2))
     f32 = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, 16, moe.MOE_EPI_STORE_F32)
-    assert np.abs(f32 - C).max() <= 1e-5 * rms
+    assert_gemm_f32_close(f32, C, "store f32")
     b16 = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, 16, moe.MOE_EPI_STORE_BF16)
     assert_bf16_close(b16.view(np.uint16), C, "store bf16")
     R = ids.size
@@ -314,11 +313,10 @@ def test_gemm_qwen_layer_rows():
     q, s = orc.quant_act(d["x"])
     sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
     C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
-    rms = np.sqrt(np.mean(C ** 2))
-    for chunk, queue in ((16, True), (16, False)):
+    for chunk, queue in ((16, True), (16, False), (64, True)):
         got = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, chunk, moe.MOE_EPI_STORE_F32,
                        queue=queue)
-        assert np.abs(got - C).max() <= 1e-5 * rms, (chunk, queue)
+        assert_gemm_f32_close(got, C, f"chunk={chunk} queue={queue}")
 
 
 # ---- stage 5: scatter --------------------------------------------------------------------
