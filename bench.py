@@ -35,6 +35,11 @@ def parse():
     p.add_argument("--static-grid", action="store_true",
                    help="walk the task list with a fixed stride instead of the atomic queue")
     p.add_argument("--chunk-rows", type=int, default=0)
+    p.add_argument("--no-graph", action="store_true",
+                   help="enqueue the kernels directly instead of replaying the cached graph")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run ten device-to-device copies of MIB MiB (a kernel of known "
+                        "traffic for scaling the HBM byte counters) and exit")
     return p.parse_args()
 
 
@@ -88,6 +93,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 10}))
+        return
     rc = moe.device_check()
     assert rc == moe.MOE_OK, f"not a gfx950 device ({rc})"
 
@@ -107,7 +121,8 @@ def main():
     wss = [ws0] + [ws0.clone() for _ in range(copies - 1)]
     out = torch.empty((M, N), dtype=torch.int16, device=dev)
     ws = torch.empty(moe.forward_workspace_bytes(M, E, k, K, N), dtype=torch.uint8, device=dev)
-    flags = moe.MOE_FWD_STATIC_GRID if args.static_grid else 0
+    flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
+        (moe.MOE_FWD_NO_GRAPH if args.no_graph else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -187,6 +202,7 @@ def main():
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
                    "task_walk": "static" if args.static_grid else "atomic queue",
+                   "launch": "plain" if args.no_graph else "graph",
                    "chunk_rows": chunk},
         "effective_tflops": round(flops / (us_layer * 1e-6) / 1e12, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],

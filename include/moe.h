@@ -109,11 +109,13 @@ int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
  *   0x7E|sign, zeros keeping their sign; an all-zero block gets scale 0 and sign-only codes.
  * Each valid route r = t*k+j takes slot = atomicAdd(cursors[topk_ids[r]], 1) and writes
  *   sorted_route_ids[slot] = r, a_q[slot][0..K) = codes of token t,
- *   a_scales[b][slot] = scale of token t, block b   (a_scales is [K/128][M*k]).
+ *   a_scales[b][slot] = scale of token t, block b   (a_scales is [K/128][M*k]),
+ *   and, when route_slots [M*k] is not NULL, route_slots[r] = slot (-1 for an invalid id).
  * The order of routes inside one expert segment depends on atomic arrival order. */
 int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
-                          int E, int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
-                          float* a_scales, moe_stream_t stream);
+                          int E, int32_t* cursors, int32_t* sorted_route_ids,
+                          int32_t* route_slots, uint8_t* a_q, float* a_scales,
+                          moe_stream_t stream);
 
 /* ---- [FMF8] problem table (128x128 blockwise weights): weight preparation ---------------
  * w f32 [E][N][K] -> w_q E4M3 [E][N][K] and w_scales f32 [E][N/128][K/128], with the
@@ -146,11 +148,14 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                      const int32_t* sorted_route_ids, void* out, moe_stream_t stream);
 
 /* ---- [FMF8] Baseline item 7 (scatter, routing-weighted) ---------------------------------
- * route_rows f32 [M*k][N] holds the GEMM row of route t*k+j (MOE_EPI_ROUTE_F32).
- *   out[t][n] = bf16( sum_{j: topk_ids[t][j] valid} topk_weights[t][j] * route_rows[t*k+j][n] )
+ * rows f32 [M*k][N] are the GEMM rows.  Route r = t*k+j reads row route_slots[r] (rows in
+ * sorted order, MOE_EPI_STORE_F32 + the slots recorded by moe_quant_sort_gather), or row r
+ * itself when route_slots is NULL (MOE_EPI_ROUTE_F32).
+ *   out[t][n] = bf16( sum_{j: topk_ids[t][j] valid} topk_weights[t][j] * row(t*k+j)[n] )
  * summed in fp32 in j order and rounded to nearest even once.  N a multiple of 4. */
-int moe_scatter(const float* route_rows, const float* topk_weights, const int32_t* topk_ids,
-                int M, int k, int E, int N, uint16_t* out, moe_stream_t stream);
+int moe_scatter(const float* rows, const int32_t* route_slots, const float* topk_weights,
+                const int32_t* topk_ids, int M, int k, int E, int N, uint16_t* out,
+                moe_stream_t stream);
 
 /* ---- whole step: route -> layout -> QSG -> FP8 grouped GEMM -> combine -------------------
  * Workspace (device, caller-owned) of at least moe_forward_workspace_bytes(...) bytes. */
@@ -158,7 +163,8 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
 
 /* Byte offset inside the workspace of one intermediate, for inspection in tests:
  * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
- * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 route_rows.  -1 on bad arguments. */
+ * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (sorted order), 12 route_slots.
+ * -1 on bad arguments. */
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
 
 /* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]

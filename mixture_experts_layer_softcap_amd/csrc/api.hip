@@ -66,8 +66,9 @@ long long max_tasks_ll(int M, int k, int E, int n_blocks, int chunk_rows) {
 }
 
 // ---- workspace of moe_forward ----------------------------------------------------------
+constexpr int kWsParts = 13;
 struct WsLayout {
-    size_t off[12];
+    size_t off[kWsParts];
     size_t total;
 };
 
@@ -77,7 +78,7 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
     const size_t R = (size_t)M * k;
     const int Nb = N / 128;
     const size_t tasks = (size_t)max_tasks_ll(M, k, E, Nb, 1);  // any chunk_rows fits
-    const size_t sz[12] = {
+    const size_t sz[kWsParts] = {
         R * 4,                      // 0 topk_ids
         R * 4,                      // 1 topk_weights
         (size_t)E * 4,              // 2 counts
@@ -89,11 +90,12 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
         R * 4,                      // 8 sorted_route_ids
         R * (size_t)K,              // 9 a_q
         (size_t)(K / 128) * R * 4,  // 10 a_scales
-        R * (size_t)N * 4,          // 11 route rows
+        R * (size_t)N * 4,          // 11 GEMM rows, sorted order
+        R * 4,                      // 12 route_slots
     };
     WsLayout L;
     size_t p = 0;
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < kWsParts; ++i) {
         L.off[i] = p;
         p = align256(p + sz[i]);
     }
@@ -142,6 +144,7 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     uint8_t* a_q = reinterpret_cast<uint8_t*>(at(9));
     float* a_s = reinterpret_cast<float*>(at(10));
     float* rows = reinterpret_cast<float*>(at(11));
+    int32_t* slots = reinterpret_cast<int32_t*>(at(12));
     const int Nb = a.N / 128;
     const int max_tasks = (int)max_tasks_ll(a.M, a.k, a.E, Nb, a.chunk);
     hipError_t e;
@@ -149,15 +152,15 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
                            max_tasks, ntasks, queue, s)) != hipSuccess)
         return e;
-    if ((e = launch_qsg(a.x, a.M, a.K, ids, a.k, a.E, cursors, sorted, a_q, a_s, s)) !=
+    if ((e = launch_qsg(a.x, a.M, a.K, ids, a.k, a.E, cursors, sorted, slots, a_q, a_s, s)) !=
         hipSuccess)
         return e;
     uint32_t* q = (a.flags & MOE_FWD_STATIC_GRID) ? nullptr : queue;
     if ((e = launch_gemm_fp8(a_q, a_s, a.M * a.k, a.K, a.w_q, a.w_scales, a.E, a.N, tasks,
-                             ntasks, max_tasks, a.chunk, q, MOE_EPI_ROUTE_F32, sorted, rows,
+                             ntasks, max_tasks, a.chunk, q, MOE_EPI_STORE_F32, nullptr, rows,
                              s)) != hipSuccess)
         return e;
-    return launch_scatter(rows, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+    return launch_scatter(rows, slots, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
 }
 
 // graph cache: one executable graph per (device, arguments)
@@ -269,15 +272,16 @@ int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
 }
 
 int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
-                          int E, int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
-                          float* a_scales, moe_stream_t stream) {
+                          int E, int32_t* cursors, int32_t* sorted_route_ids,
+                          int32_t* route_slots, uint8_t* a_q, float* a_scales,
+                          moe_stream_t stream) {
     if (!route_dims_ok(M, E, k) || K < 128 || K % 128) return MOE_E_INVAL;
     if (M > 0 && (!x || !topk_ids || !cursors || !sorted_route_ids || !a_q || !a_scales))
         return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
-    return hip_status(launch_qsg(x, M, K, topk_ids, k, E, cursors, sorted_route_ids, a_q,
-                                 a_scales, (hipStream_t)stream));
+    return hip_status(launch_qsg(x, M, K, topk_ids, k, E, cursors, sorted_route_ids,
+                                 route_slots, a_q, a_scales, (hipStream_t)stream));
 }
 
 int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, float* w_scales,
@@ -315,13 +319,14 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                                       sorted_route_ids, out, (hipStream_t)stream));
 }
 
-int moe_scatter(const float* route_rows, const float* topk_weights, const int32_t* topk_ids,
-                int M, int k, int E, int N, uint16_t* out, moe_stream_t stream) {
+int moe_scatter(const float* rows, const int32_t* route_slots, const float* topk_weights,
+                const int32_t* topk_ids, int M, int k, int E, int N, uint16_t* out,
+                moe_stream_t stream) {
     if (!route_dims_ok(M, E, k) || N < 4 || N % 4) return MOE_E_INVAL;
-    if (M > 0 && (!route_rows || !topk_weights || !topk_ids || !out)) return MOE_E_INVAL;
+    if (M > 0 && (!rows || !topk_weights || !topk_ids || !out)) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
-    return hip_status(launch_scatter(route_rows, topk_weights, topk_ids, M, k, E, N, out,
+    return hip_status(launch_scatter(rows, route_slots, topk_weights, topk_ids, M, k, E, N, out,
                                      (hipStream_t)stream));
 }
 
@@ -331,7 +336,7 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N) {
 }
 
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which) {
-    if (!forward_dims_ok(M, E, k, K, N) || which < 0 || which >= 12) return -1;
+    if (!forward_dims_ok(M, E, k, K, N) || which < 0 || which >= kWsParts) return -1;
     return (int64_t)ws_layout(M, E, k, K, N).off[which];
 }
 

@@ -23,8 +23,8 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
                          int max_tasks, int32_t* ntasks, uint32_t* queue, hipStream_t s);
 
 hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
-                      int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
-                      float* a_scales, hipStream_t s);
+                      int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,
+                      uint8_t* a_q, float* a_scales, hipStream_t s);
 
 hipError_t launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q,
                                    float* w_scales, hipStream_t s);
@@ -35,7 +35,16 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, in
                            int chunk_rows, uint32_t* queue, int epilogue,
                            const int32_t* sorted_route_ids, void* out, hipStream_t s);
 
-hipError_t launch_scatter(const float* rows, const float* weights, const int32_t* ids, int M,
-                          int k, int E, int N, uint16_t* out, hipStream_t s);
+// streaming form for tasks of at most 16 routed rows and K = 2048
+bool gemm_fp8_stream_applies(int K, int chunk_rows);
+hipError_t launch_gemm_fp8_stream(const uint8_t* a, const float* a_scales, int rows, int K,
+                                  const uint8_t* w, const float* w_scales, int N,
+                                  const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                                  uint32_t* queue, int epilogue, const int32_t* sorted,
+                                  void* out, hipStream_t s);
+
+hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
+                          const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
+                          hipStream_t s);
 
 }  // namespace moe

@@ -48,7 +48,7 @@ __device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
 __global__ __launch_bounds__(kThreads) void qsg_kernel(
     const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ ids, int k, int E,
     int32_t* __restrict__ cursors, int32_t* __restrict__ sorted_route_ids,
-    uint8_t* __restrict__ a_q, float* __restrict__ a_scales) {
+    int32_t* __restrict__ route_slots, uint8_t* __restrict__ a_q, float* __restrict__ a_scales) {
     __shared__ int s_slot[64];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void qsg_kernel(
             sorted_route_ids[slot] = r;
         }
         s_slot[tid] = slot;
+        if (route_slots) route_slots[r] = slot;
     }
     __syncthreads();
 
@@ -93,11 +94,11 @@ __global__ __launch_bounds__(kThreads) void qsg_kernel(
 }  // namespace
 
 hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
-                      int32_t* cursors, int32_t* sorted_route_ids, uint8_t* a_q,
-                      float* a_scales, hipStream_t s) {
+                      int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,
+                      uint8_t* a_q, float* a_scales, hipStream_t s) {
     if (M == 0) return hipSuccess;
     hipLaunchKernelGGL(qsg_kernel, dim3(M), dim3(kThreads), 0, s, x, M, K, ids, k, E, cursors,
-                       sorted_route_ids, a_q, a_scales);
+                       sorted_route_ids, route_slots, a_q, a_scales);
     return hipGetLastError();
 }
 

@@ -2,10 +2,11 @@
 // ([FMF8] "Baseline: 7 kernels" item 7 and Fusion 1: token = route_id / TOPK,
 // weight = topk_weights[token, route_id % TOPK], output[token] += weight * row).
 //
-// The GEMM epilogue writes each routed row at its route id t*k+j (plain 16-byte stores), so
-// the scatter-add becomes a gather-sum per token: out[t] = bf16(sum_j w[t][j] * row[t*k+j]),
-// summed in fp32 in j order.  No float atomics, no zero-initialised accumulator, and the
-// result does not depend on the order of rows inside an expert segment.
+// The GEMM writes its fp32 rows with plain 16-byte stores (in sorted order, or at the route
+// id), and the scatter-add becomes a gather-sum per token:
+// out[t] = bf16(sum_j w[t][j] * row(t*k+j)), summed in fp32 in j order.  No float atomics,
+// no zero-initialised accumulator, and the result does not depend on the order of rows
+// inside an expert segment.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -15,8 +16,9 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
-    const float* __restrict__ rows, const float* __restrict__ weights,
-    const int32_t* __restrict__ ids, int M, int k, int E, int N, uint16_t* __restrict__ out) {
+    const float* __restrict__ rows, const int32_t* __restrict__ route_slots,
+    const float* __restrict__ weights, const int32_t* __restrict__ ids, int M, int k, int E,
+    int N, uint16_t* __restrict__ out) {
     const int quads = N >> 2;
     const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= (size_t)M * quads) return;
@@ -26,8 +28,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     for (int j = 0; j < k; ++j) {
         const size_t r = (size_t)t * k + j;
         if ((unsigned)ids[r] >= (unsigned)E) continue;
+        const size_t row = route_slots ? (size_t)route_slots[r] : r;
         const float w = weights[r];
-        const float4 v = *reinterpret_cast<const float4*>(rows + r * N + n);
+        const float4 v = *reinterpret_cast<const float4*>(rows + row * N + n);
         acc.x += w * v.x;
         acc.y += w * v.y;
         acc.z += w * v.z;
@@ -41,13 +44,14 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
 
 }  // namespace
 
-hipError_t launch_scatter(const float* rows, const float* weights, const int32_t* ids, int M,
-                          int k, int E, int N, uint16_t* out, hipStream_t s) {
+hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
+                          const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
+                          hipStream_t s) {
     const size_t work = (size_t)M * (N / 4);
     if (work == 0) return hipSuccess;
     const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(scatter_kernel, dim3(grid), dim3(kThreads), 0, s, rows, weights, ids, M,
-                       k, E, N, out);
+    hipLaunchKernelGGL(scatter_kernel, dim3(grid), dim3(kThreads), 0, s, rows, route_slots,
+                       weights, ids, M, k, E, N, out);
     return hipGetLastError();
 }
 

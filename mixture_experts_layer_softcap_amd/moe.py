@@ -38,12 +38,12 @@ SIGNATURES = {
     "moe_route": (_I, [_P, _I, _I, _I, _F, _P, _P, _P]),
     "moe_max_tasks": (_I, [_I, _I, _I, _I, _I]),
     "moe_build_layout": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
-    "moe_quant_sort_gather": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_quant_sort_gather": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_gemm_n_tile": (_I, [_I]),
     "moe_grouped_gemm": (_I, [_I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I,
                               _P, _P, _P]),
-    "moe_scatter": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
@@ -124,11 +124,12 @@ def build_layout(topk_ids, E: int, n_blocks: int, chunk_rows: int, counts, offse
 
 
 def quant_sort_gather(x, topk_ids, E: int, cursors, sorted_route_ids, a_q, a_scales,
-                      stream=None):
+                      route_slots=None, stream=None):
     M, K = x.shape
     k = topk_ids.shape[1]
     _call("moe_quant_sort_gather", _ptr(x), M, K, _ptr(topk_ids), k, E, _ptr(cursors),
-          _ptr(sorted_route_ids), _ptr(a_q), _ptr(a_scales), _stream(stream))
+          _ptr(sorted_route_ids), _ptr(route_slots), _ptr(a_q), _ptr(a_scales),
+          _stream(stream))
 
 
 def quantize_weights(w, w_q, w_scales, stream=None):
@@ -149,11 +150,11 @@ def grouped_gemm(mode: int, a, a_scales, w, w_scales, tasks, ntasks, chunk_rows:
           _ptr(sorted_route_ids), _ptr(out), _stream(stream))
 
 
-def scatter(route_rows, topk_weights, topk_ids, E: int, out, stream=None):
+def scatter(rows, topk_weights, topk_ids, E: int, out, route_slots=None, stream=None):
     M, k = topk_ids.shape
-    N = route_rows.shape[1]
-    _call("moe_scatter", _ptr(route_rows), _ptr(topk_weights), _ptr(topk_ids), M, k, E, N,
-          _ptr(out), _stream(stream))
+    N = rows.shape[1]
+    _call("moe_scatter", _ptr(rows), _ptr(route_slots), _ptr(topk_weights), _ptr(topk_ids), M,
+          k, E, N, _ptr(out), _stream(stream))
 
 
 def forward_workspace_bytes(M: int, E: int, k: int, K: int, N: int) -> int:

@@ -57,10 +57,10 @@ def test_workspace_queries(L):
     b = L.moe_forward_workspace_bytes(128, 256, 8, 2048, 512)
     R = 128 * 8
     assert b >= R * 2048 + R * 512 * 4 + 16 * 4 * R
-    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(12)]
+    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(13)]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < b
     assert L.moe_forward_workspace_bytes(128, 256, 8, 2000, 512) == 0   # K % 128
-    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 12) == -1
+    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 13) == -1
 
 
 NULL = None
@@ -79,8 +79,8 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert L.moe_build_layout(P, 16, 2, 8, 2, 4, P, P, P, P, need - 1, P, P, S) == NOSPC
     assert L.moe_build_layout(P, 16, 2, 8, 2, 2000, P, P, P, P, 10 ** 6, P, P, S) == INVAL
     assert L.moe_build_layout(P, 16, 2, 8, 2, 4, NULL, P, P, P, need, P, P, S) == INVAL
-    assert L.moe_quant_sort_gather(P, 4, 200, P, 2, 8, P, P, P, P, S) == INVAL   # K % 128
-    assert L.moe_quant_sort_gather(P, 4, 256, NULL, 2, 8, P, P, P, P, S) == INVAL
+    assert L.moe_quant_sort_gather(P, 4, 200, P, 2, 8, P, P, P, P, P, S) == INVAL  # K % 128
+    assert L.moe_quant_sort_gather(P, 4, 256, NULL, 2, 8, P, P, P, P, P, S) == INVAL
     assert L.moe_quantize_weights(P, 2, 100, 256, P, P, S) == INVAL
     assert L.moe_quantize_weights(NULL, 2, 128, 256, P, P, S) == INVAL
     gg = L.moe_grouped_gemm
@@ -89,7 +89,7 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 9, P, P, S) == INVAL  # epilogue
     assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 2, NULL, P, S) == INVAL  # route ids
     assert gg(0, P, P, 4, 250, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # K % 128
-    assert L.moe_scatter(P, P, P, 4, 2, 8, 6, P, S) == INVAL          # N % 4
+    assert L.moe_scatter(P, P, P, P, 4, 2, 8, 6, P, S) == INVAL       # N % 4
     ws = L.moe_forward_workspace_bytes(8, 16, 2, 256, 256)
     f = L.moe_forward_ex
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC

@@ -269,11 +269,14 @@ def gpu_gemm(a_q, a_s, w_q, w_s, offsets, chunk, epilogue, sorted_ids=None, queu
     return to_np(out)
 
 
-@pytest.mark.parametrize("chunk,queue", [(16, True), (16, False), (32, True), (64, True),
-                                         (5, True)])
-def test_gemm_integer_exact(chunk, queue):
-    g = np.random.default_rng(chunk)
-    E, N, K = 4, 256, 512
+@pytest.mark.parametrize("chunk,queue,K", [(16, True, 512), (16, False, 512), (32, True, 512),
+                                           (64, True, 512), (5, True, 512), (16, True, 2048),
+                                           (16, False, 2048), (7, False, 4096),
+                                           (3, True, 4096), (64, False, 2048)])
+def test_gemm_integer_exact(chunk, queue, K):
+    # K in {2048, 4096} with chunk <= 16 takes the streaming kernel, the rest the general one
+    g = np.random.default_rng(chunk + K)
+    E, N = 4, 256
     counts = np.array([3, 0, 37, 70], np.int32)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(offsets[-1])
