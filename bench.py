@@ -2,8 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one whole forward (route -> layout -> QSG -> FP8 grouped GEMM -> combine), replayed
-from the library's cached HIP graph, on the Qwen3.5-35B-A3B-shaped layer of the Fused MoE
+A step is one whole forward (route -> layout -> QSG -> FP8 grouped GEMM -> combine), enqueued
+as plain kernel launches (--graph replays the library's cached HIP graph instead), on the
+Qwen3.5-35B-A3B-shaped layer of the Fused MoE
 FP8 tutorial's problem table: M=128 tokens, 256 experts, top-8, K=2048, N=512.  Inputs are
 seeded synthetic data resident in HBM before timing; the weights are rotated over enough
 copies (>= 1 GiB) that every step streams them from HBM rather than from the 256 MB
@@ -35,12 +36,33 @@ def parse():
     p.add_argument("--static-grid", action="store_true",
                    help="walk the task list with a fixed stride instead of the atomic queue")
     p.add_argument("--chunk-rows", type=int, default=0)
-    p.add_argument("--no-graph", action="store_true",
-                   help="enqueue the kernels directly instead of replaying the cached graph")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the cached HIP graph of the step instead of launching its kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run ten device-to-device copies of MIB MiB (a kernel of known "
                         "traffic for scaling the HBM byte counters) and exit")
     return p.parse_args()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the timed grouped GEMM from the committed rocprofv3 counter
+    record (FETCH_SIZE + WRITE_SIZE, copy-calibrated) for this workload, or None when there is
+    none or the kernel's source has changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.json"))):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src):
+            continue
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == rec["source_sha256"]:
+                return rec["traffic_bytes"]
+    return None
 
 
 def gemm_algorithmic_bytes(counts, M, k, K, N):
@@ -122,7 +144,7 @@ def main():
     out = torch.empty((M, N), dtype=torch.int16, device=dev)
     ws = torch.empty(moe.forward_workspace_bytes(M, E, k, K, N), dtype=torch.uint8, device=dev)
     flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
-        (moe.MOE_FWD_NO_GRAPH if args.no_graph else 0)
+        (moe.MOE_FWD_GRAPH if args.graph else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -201,17 +223,22 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
-                   "task_walk": "static" if args.static_grid else "atomic queue",
-                   "launch": "plain" if args.no_graph else "graph",
+                   "gemm_task_walk": ("contiguous ranges, per-wave pull" if K == 2048 and chunk <= 16
+                                      else "static stride" if args.static_grid else "atomic queue"),
+                   "launch": "graph" if args.graph else "plain",
                    "chunk_rows": chunk},
         "effective_tflops": round(flops / (us_layer * 1e-6) / 1e12, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
         "layer_hbm_frac": round(lbytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_algorithmic_bytes": lbytes,
         "nonempty_experts": int((counts > 0).sum()),
-        "roofline": {"bound": "hbm", "kernel": "gemm_fp8_kernel (grouped FP8 GEMM)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("gemm_fp8_range_kernel" if K == 2048 and chunk <= 16
+                                else "gemm_fp8_kernel") + " (grouped FP8 GEMM, ROUTE_F32)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload)
+                     if K == 2048 and chunk <= 16 else None,
                      "algorithmic_bytes_per_launch": gbytes,
                      "avg_launch_us": round(gemm_us, 3)},
     }

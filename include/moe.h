@@ -169,16 +169,17 @@ int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int whic
 
 /* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]
  * -> out bf16 [M][N].  K, N multiples of 128.
- * The five stages are enqueued on `stream` with no host synchronisation.  Unless the stream
- * is being captured by the caller, the sequence is captured once into a HIP graph per
- * (shape, softcap, pointers, options) and replayed on later calls. */
+ * The five stages are enqueued on `stream` as plain kernel launches, with no host
+ * synchronisation (moe_forward_ex can replay a cached HIP graph instead). */
 int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
                 const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                 uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
-/* moe_forward with explicit options: chunk_rows (0 = chosen from M*k/E), flags bit 0 = no
- * graph (plain launches), bit 1 = fixed-stride task walk instead of the atomic queue. */
-#define MOE_FWD_NO_GRAPH 1
+/* moe_forward with explicit options: chunk_rows (0 = chosen from M*k/E), flags bit 0 = replay
+ * a HIP graph captured once per (shape, softcap, pointers, options) instead of launching the
+ * kernels (ignored while the caller's stream is being captured), bit 1 = fixed-stride task
+ * walk instead of the atomic queue (grouped GEMM forms that walk a queue). */
+#define MOE_FWD_GRAPH 1
 #define MOE_FWD_STATIC_GRID 2
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,

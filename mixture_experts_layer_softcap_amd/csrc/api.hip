@@ -348,7 +348,7 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     if (!logits || !x || !w_q || !w_scales || !out || !workspace) return MOE_E_INVAL;
     if (softcap != softcap) return MOE_E_INVAL;
     if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
-    if (flags & ~(MOE_FWD_NO_GRAPH | MOE_FWD_STATIC_GRID)) return MOE_E_INVAL;
+    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID)) return MOE_E_INVAL;
     if (workspace_bytes < ws_layout(M, E, k, K, N).total) return MOE_E_NOSPC;
     int rc = check_device();
     if (rc) return rc;
@@ -360,7 +360,7 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
         (void)hipGetLastError();
         return MOE_E_HIP;
     }
-    if ((flags & MOE_FWD_NO_GRAPH) || cs != hipStreamCaptureStatusNone)
+    if (!(flags & MOE_FWD_GRAPH) || cs != hipStreamCaptureStatusNone)
         return hip_status(enqueue_forward(a, s));
     return forward_graph(a, s);
 }

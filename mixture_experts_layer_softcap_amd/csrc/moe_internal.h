@@ -35,13 +35,13 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, in
                            int chunk_rows, uint32_t* queue, int epilogue,
                            const int32_t* sorted_route_ids, void* out, hipStream_t s);
 
-// streaming form for tasks of at most 16 routed rows and K = 2048
-bool gemm_fp8_stream_applies(int K, int chunk_rows);
-hipError_t launch_gemm_fp8_stream(const uint8_t* a, const float* a_scales, int rows, int K,
-                                  const uint8_t* w, const float* w_scales, int N,
-                                  const moe_task* tasks, const int32_t* ntasks, int max_tasks,
-                                  uint32_t* queue, int epilogue, const int32_t* sorted,
-                                  void* out, hipStream_t s);
+// contiguous-range form for tasks of at most 16 routed rows and K = 2048
+bool gemm_fp8_range_applies(int K, int chunk_rows);
+hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int rows, int K,
+                                 const uint8_t* w, const float* w_scales, int N,
+                                 const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                                 int epilogue, const int32_t* sorted, void* out,
+                                 hipStream_t s);
 
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,

@@ -27,7 +27,7 @@ MOE_EPI_STORE_BF16 = 1
 MOE_EPI_ROUTE_F32 = 2
 MOE_EPI_SWIGLU_BF16 = 3
 
-MOE_FWD_NO_GRAPH = 1
+MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
 
 # entry points and their C signatures (names identical to include/moe.h)

@@ -363,7 +363,7 @@ def ws_part(ws, d, which, dtype, count):
     return to_np(ws[off:off + nbytes]).view(dtype)
 
 
-@pytest.mark.parametrize("flags", [0, moe.MOE_FWD_NO_GRAPH, moe.MOE_FWD_STATIC_GRID])
+@pytest.mark.parametrize("flags", [0, moe.MOE_FWD_GRAPH, moe.MOE_FWD_STATIC_GRID])
 @pytest.mark.parametrize("name", [TINY, QWEN])
 def test_forward_full(name, flags):
     d = workload(name)
