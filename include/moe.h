@@ -135,12 +135,15 @@ int moe_gemm_n_tile(int mode);
  * and the epilogue writes h (see MOE_EPI_*).  a is [rows][K] (u8 or bf16); w is [E][N][K].
  * a_scales/w_scales are ignored in BF16 mode.  sorted_route_ids [rows] is read only by
  * MOE_EPI_ROUTE_F32 (may be NULL otherwise).
- * Scheduling: with queue != NULL, a persistent grid pulls task indices from queue[0] with
- * atomics; the last workgroup to leave resets queue[0..1] to zero, so the call can be
- * repeated or graph-replayed.  With queue == NULL, the same grid walks the task list with a
- * fixed stride.  Tasks must come from moe_build_layout for the same rows, E, n_tile and
- * chunk_rows (FP8_B128: chunk_rows <= 64).  The expert weights are streamed once per task,
- * so every task of the same expert re-reads its panel (from HBM or the caches). */
+ * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 2048 the task list is cut into one
+ * contiguous range of 16-column subtasks per workgroup, balanced inside the workgroup by an
+ * LDS counter; queue is not used.  Otherwise, with queue != NULL, a persistent grid pulls
+ * task indices from queue[0] with atomics and the last workgroup to leave resets
+ * queue[0..1] to zero, so the call can be repeated or graph-replayed; with queue == NULL
+ * the same grid walks the task list with a fixed stride.  Tasks must come from
+ * moe_build_layout for the same rows, E, n_tile and chunk_rows (chunk_rows <= 64): all
+ * n_blocks panels of one chunk consecutive.  Each task streams its expert's 128-column
+ * weight panel once. */
 int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
                      const void* w, const float* w_scales, int E, int N,
                      const moe_task* tasks, const int32_t* ntasks, int max_tasks,
