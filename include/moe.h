@@ -124,7 +124,9 @@ int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, floa
                          moe_stream_t stream);
 
 /* ---- [FMF8] Baseline item 6 (grouped GEMM) + [WEAVE] persistent atomic task queue -------
- * Output column tile of one task, per operand mode: 128 for MOE_GEMM_FP8_B128. */
+ * Output column tile of one task, per operand mode: 128 for MOE_GEMM_FP8_B128, 256 for
+ * MOE_GEMM_BF16 (with MOE_EPI_SWIGLU_BF16 a task's 256 weight rows are 128 gate rows and
+ * their 128 up rows, giving 128 output columns).  -1 for an unknown mode. */
 int moe_gemm_n_tile(int mode);
 
 /* For every task (e, r0, nr, nb) in tasks[0..*ntasks) and every row r in [r0, r0+nr),
@@ -135,15 +137,21 @@ int moe_gemm_n_tile(int mode);
  * and the epilogue writes h (see MOE_EPI_*).  a is [rows][K] (u8 or bf16); w is [E][N][K].
  * a_scales/w_scales are ignored in BF16 mode.  sorted_route_ids [rows] is read only by
  * MOE_EPI_ROUTE_F32 (may be NULL otherwise).
+ * BF16 mode ([H200] gated-up and down projections; [WEAVE] Mixtral-like layer): K a multiple
+ * of 64, N a multiple of 256, chunk_rows <= 256; epilogues STORE_F32, STORE_BF16 and
+ * SWIGLU_BF16, which writes out [rows][N/2] bf16 = bf16(silu(h[:, c]) * h[:, N/2 + c]) for
+ * the task's 128 columns c (weight rows [0, N/2) are the gate, [N/2, N) the up projection).
+ * One 256 x 256 output tile per task and workgroup (grid = max_tasks; workgroups past
+ * *ntasks exit at once); queue is not used.
  * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 2048 the task list is cut into one
  * contiguous range of 16-column subtasks per workgroup, balanced inside the workgroup by an
  * LDS counter; queue is not used.  Otherwise, with queue != NULL, a persistent grid pulls
  * task indices from queue[0] with atomics and the last workgroup to leave resets
  * queue[0..1] to zero, so the call can be repeated or graph-replayed; with queue == NULL
  * the same grid walks the task list with a fixed stride.  Tasks must come from
- * moe_build_layout for the same rows, E, n_tile and chunk_rows (chunk_rows <= 64): all
- * n_blocks panels of one chunk consecutive.  Each task streams its expert's 128-column
- * weight panel once. */
+ * moe_build_layout for the same rows, E, n_tile and chunk_rows (FP8_B128: chunk_rows <= 64):
+ * all n_blocks panels of one chunk consecutive.  Each task streams its expert's weight panel
+ * once. */
 int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
                      const void* w, const float* w_scales, int E, int N,
                      const moe_task* tasks, const int32_t* ntasks, int max_tasks,

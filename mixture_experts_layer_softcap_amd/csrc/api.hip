@@ -294,13 +294,31 @@ int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, floa
     return hip_status(launch_quantize_weights(w, E, N, K, w_q, w_scales, (hipStream_t)stream));
 }
 
-int moe_gemm_n_tile(int mode) { return mode == MOE_GEMM_FP8_B128 ? 128 : -1; }
+int moe_gemm_n_tile(int mode) {
+    return mode == MOE_GEMM_FP8_B128 ? 128 : mode == MOE_GEMM_BF16 ? 256 : -1;
+}
 
 int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
                      const void* w, const float* w_scales, int E, int N,
                      const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                      int chunk_rows, uint32_t* queue, int epilogue,
                      const int32_t* sorted_route_ids, void* out, moe_stream_t stream) {
+    if (mode == MOE_GEMM_BF16) {
+        if (rows < 0 || E < 1 || K < 64 || K % 64 || N < 256 || N % 256 || max_tasks < 0)
+            return MOE_E_INVAL;
+        if (chunk_rows < 1 || chunk_rows > 256) return MOE_E_INVAL;
+        if (epilogue != MOE_EPI_STORE_F32 && epilogue != MOE_EPI_STORE_BF16 &&
+            epilogue != MOE_EPI_SWIGLU_BF16)
+            return MOE_E_INVAL;
+        if (!w || !ntasks || !out || (max_tasks > 0 && !tasks)) return MOE_E_INVAL;
+        if (rows > 0 && !a) return MOE_E_INVAL;
+        if ((long long)E * N * K > (1ll << 40)) return MOE_E_INVAL;
+        int rc = check_device();
+        if (rc) return rc;
+        return hip_status(launch_gemm_bf16(static_cast<const uint16_t*>(a), K,
+                                           static_cast<const uint16_t*>(w), N, tasks, ntasks,
+                                           max_tasks, epilogue, out, (hipStream_t)stream));
+    }
     if (mode != MOE_GEMM_FP8_B128) return MOE_E_INVAL;
     if (rows < 0 || E < 1 || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
         return MOE_E_INVAL;

@@ -43,6 +43,11 @@ hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int ro
                                  int epilogue, const int32_t* sorted, void* out,
                                  hipStream_t s);
 
+// BF16 grouped GEMM (256 x 256 tiles; STORE_F32, STORE_BF16, SWIGLU_BF16)
+hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
+                            const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                            int epilogue, void* out, hipStream_t s);
+
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
                           hipStream_t s);

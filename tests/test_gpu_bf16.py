@@ -1,0 +1,139 @@
+"""GPU parity of the BF16 grouped GEMM (large routed-row counts) against the CPU oracle.
+
+The oracle computes every output in double from the bf16 operands.  fp32 outputs are held to
+a tolerance derived from the arithmetic: bf16 x bf16 products are exact in fp32 and the matrix
+core accumulates in fp32, so the error is a few fp32 roundings per 16-wide k step
+(GEMM_BF16_F32_*).  bf16 stores use the BF16 output bar and lie within one bf16 ulp of the
+oracle's own bf16 rounding; SwiGLU outputs are held to their bf16 rounding per element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mixture_experts_layer_softcap_amd import moe, synth
+
+from gpu_util import assert_bf16_close, bf16_f64, to_dev, to_np, zeros
+
+pytestmark = pytest.mark.gpu
+
+# fp32 rows against the double oracle: K/16 fp32 accumulations of exact products
+GEMM_BF16_F32_REL_FRO = 2e-5
+GEMM_BF16_F32_ELEM_RMS = 2e-4
+CHUNK = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc.build(force=False)
+    assert moe.device_check() == moe.MOE_OK
+
+
+def layout_for_counts(counts, n_blocks, chunk=CHUNK):
+    """Task list for expert-contiguous rows with these per-expert counts (k = 1 routing)."""
+    counts = np.asarray(counts, np.int32)
+    E = counts.shape[0]
+    rows = int(counts.sum())
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)
+    mt = moe.max_tasks(rows, 1, E, n_blocks, chunk)
+    dev = dict(counts=zeros((E,), torch.int32), offsets=zeros((E + 1,), torch.int32),
+               cursors=zeros((E,), torch.int32), tasks=zeros((max(mt, 1), 4), torch.int32),
+               ntasks=zeros((1,), torch.int32), queue=zeros((2,), torch.int32))
+    moe.build_layout(to_dev(ids), E, n_blocks, chunk, dev["counts"], dev["offsets"],
+                     dev["cursors"], dev["tasks"], dev["ntasks"], dev["queue"])
+    return dev
+
+
+def run_gemm(A, W, counts, epilogue, out_cols=None):
+    rows, K = A.shape
+    E, N, _ = W.shape
+    lay = layout_for_counts(counts, N // moe.gemm_n_tile(moe.MOE_GEMM_BF16))
+    cols = N if out_cols is None else out_cols
+    dt = torch.float32 if epilogue == moe.MOE_EPI_STORE_F32 else torch.int16
+    out = zeros((rows, cols), dt)
+    moe.grouped_gemm(moe.MOE_GEMM_BF16, to_dev(A), None, to_dev(W), None, lay["tasks"],
+                     lay["ntasks"], CHUNK, out, epilogue)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(lay["counts"]), counts)
+    return to_np(out, None if dt == torch.float32 else np.uint16)
+
+
+def assert_f32_close(y, ref, what=""):
+    ref = np.asarray(ref, np.float64)
+    y = np.asarray(y, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    fro = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+    worst = float(np.abs(y - ref).max())
+    assert fro <= GEMM_BF16_F32_REL_FRO, f"{what}: rel Frobenius {fro:.3e}"
+    assert worst <= GEMM_BF16_F32_ELEM_RMS * rms, f"{what}: max |d| {worst:.3e} vs rms {rms:.3e}"
+
+
+def inputs(rows, E, N, K, dist, seed=0, counts=None):
+    d = synth.grouped_gemm_inputs(rows, E, N, K, dist, seed=seed)
+    if counts is not None:
+        d["counts"] = np.asarray(counts, np.int32)
+        d["offsets"] = np.concatenate([[0], np.cumsum(d["counts"])]).astype(np.int32)
+    return d
+
+
+@pytest.mark.parametrize("rows,E,N,K,dist", [
+    (700, 5, 512, 192, "random"),      # chunks of 256 + partial chunks, K of 3 steps
+    (513, 3, 256, 64, "skewed"),       # one k step; a 1-row tail chunk likely
+    (300, 4, 768, 1024, "balanced"),   # 16 k steps, three column panels
+])
+def test_bf16_gemm_f32_matches_oracle(rows, E, N, K, dist):
+    d = inputs(rows, E, N, K, dist, seed=rows)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_F32)
+    _, ref = orc.gemm_bf16(d["A"], d["W"], d["offsets"])
+    assert_f32_close(y, ref, f"rows={rows}")
+
+
+def test_bf16_gemm_bf16_store_and_edge_counts():
+    # an empty expert, a single-row expert, a 31-row expert and one just over a chunk
+    counts = [0, 1, 31, 257]
+    d = inputs(sum(counts), 4, 512, 128, "balanced", seed=3, counts=counts)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_BF16)
+    bits, ref = orc.gemm_bf16(d["A"], d["W"], d["offsets"])
+    assert_bf16_close(y, ref, "bf16 store")
+    # bf16 of the fp32 accumulation lies within one bf16 ulp of the oracle's bf16(double)
+    diff = np.abs(bf16_f64(y) - bf16_f64(bits))
+    ulp = np.abs(bf16_f64(bits)) * 2.0 ** -7 + 1e-30
+    assert (diff <= ulp).all()
+
+
+def test_bf16_gemm_swiglu_epilogue():
+    rows, E, N, K = 600, 3, 512, 256       # gate rows [0, 256), up rows [256, 512)
+    d = inputs(rows, E, N, K, "random", seed=11)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_SWIGLU_BF16, out_cols=N // 2)
+    _, h = orc.gemm_bf16(d["A"], d["W"], d["offsets"])
+    g, u = h[:, : N // 2], h[:, N // 2:]
+    ref = g / (1.0 + np.exp(-g)) * u
+    # The product is heavy-tailed (its largest entries are tens of rms), so the bound per
+    # element is the bf16 rounding itself (RNE: 2^-9 relative; 2^-8 leaves room for the fp32
+    # accumulation and fp32 silu) plus a small absolute term for entries near zero, and the
+    # Frobenius part of the BF16 output bar.
+    yv = bf16_f64(y)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bad = np.abs(yv - ref) > 2.0 ** -8 * np.abs(ref) + 1e-5 * rms
+    assert not bad.any(), f"swiglu: {int(bad.sum())} entries beyond bf16 rounding"
+    fro = float(np.linalg.norm(yv - ref) / np.linalg.norm(ref))
+    assert fro <= 5e-3, f"swiglu: relative Frobenius {fro:.3e}"
+
+
+def test_bf16_gemm_full_up_projection_sampled():
+    # the gated-up projection at 4096 routed rows, E=16, H=3072, I=1536 (Dirichlet(1) rows);
+    # the oracle checks every expert's first and last row plus a seeded sample
+    rows, E, N, K = 4096, 16, 3072, 3072
+    d = inputs(rows, E, N, K, "random", seed=0)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_F32)
+    off = d["offsets"]
+    pick = set()
+    for e in range(E):
+        if d["counts"][e]:
+            pick.update((int(off[e]), int(off[e + 1]) - 1))
+    pick.update(np.random.default_rng(5).choice(rows, 32, replace=False).tolist())
+    rl = np.array(sorted(pick), np.int32)
+    _, ref = orc.gemm_bf16(d["A"], d["W"], off, rows_list=rl)
+    assert_f32_close(y[rl], ref, "up projection sample")
