@@ -100,6 +100,75 @@ def cpu_baseline(d, k, cap, budget_s=12.0):
                       f"median of {len(times)} runs; host has {os.cpu_count()} cores"}
 
 
+# BF16 grouped GEMMs of the gated-up and down projections over compact routed rows (E=16,
+# H=3072, I=1536: up [rows,3072] x [3072,3072], down [rows,1536] x [1536,3072]).
+BF16_GEMMS = {"up": (3072, 3072), "down": (3072, 1536)}   # N, K
+BF16_DENSE_PEAK_TFLOPS = 2500.0                          # MI355X dense BF16 MFMA, published
+
+
+def bench_bf16_gemm(args, moe, synth, torch, np):
+    """--workload bf16_grouped_gemm_<up|down>_rows<R>_<balanced|random|skewed>: one grouped
+    GEMM per step (tasks built once, outside timing), fp32 accumulate, bf16 out."""
+    _, _, _, proj, rows_s, dist = args.workload.split("_")
+    N, K = BF16_GEMMS[proj]
+    rows, E, chunk = int(rows_s[4:]), 16, 256
+    d = synth.grouped_gemm_inputs(rows, E, N, K, dist, seed=0)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(d["A"].view(np.int16)).to(dev)
+    w0 = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+    copies = max(1, -(-WEIGHT_BYTES_ROTATION // (w0.numel() * 2)))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    counts = d["counts"]
+    ids = torch.from_numpy(np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)).to(dev)
+    nb = N // moe.gemm_n_tile(moe.MOE_GEMM_BF16)
+    mt = moe.max_tasks(rows, 1, E, nb, chunk)
+    z = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)
+    cnt, off, cur, ntasks, queue = z(E), z(E + 1), z(E), z(1), z(2)
+    tasks = z(mt * 4).view(mt, 4)
+    moe.build_layout(ids, E, nb, chunk, cnt, off, cur, tasks, ntasks, queue)
+    out = torch.empty((rows, N), dtype=torch.int16, device=dev)
+
+    def step(i):
+        moe.grouped_gemm(moe.MOE_GEMM_BF16, a, None, ws[i % copies], None, tasks, ntasks, chunk,
+                         out, moe.MOE_EPI_STORE_BF16)
+
+    for i in range(max(args.warmup, copies)):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+    flops = 2.0 * rows * N * K
+    tflops = flops / (us * 1e-6) / 1e12
+    nonempty = int((counts > 0).sum())
+    gbytes = rows * K * 2 + nonempty * N * K * 2 + rows * N * 2
+    result = {
+        "metric": "µs per BF16 grouped GEMM + TFLOPS & %MFMA peak",
+        "value": round(us, 3), "unit": "us/gemm", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "E": E, "N": N, "K": K,
+                   "row_distribution": dist, "nonempty_experts": nonempty, "chunk_rows": chunk,
+                   "max_expert_rows": int(counts.max()), "weight_copies_rotated": copies},
+        "effective_tflops": round(tflops, 2),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (STORE_BF16)",
+                     "achieved": round(tflops, 2), "peak": BF16_DENSE_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": gbytes,
+                     "hbm_frac": round(gbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(us, 3)},
+    }
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +196,9 @@ def main():
     rc = moe.device_check()
     assert rc == moe.MOE_OK, f"not a gfx950 device ({rc})"
 
+    if args.workload.startswith("bf16_grouped_gemm_"):
+        bench_bf16_gemm(args, moe, synth, torch, np)
+        return
     d = synth.workload_inputs(args.workload)
     M, E, k, K, N, cap = d["M"], d["E"], d["k"], d["K"], d["N"], d["cap"]
 

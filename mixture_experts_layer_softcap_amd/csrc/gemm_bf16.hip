@@ -10,10 +10,10 @@
 // so a lane holds, for one routed row, runs of 4 consecutive output columns.  Per 16-wide k
 // step a wave reads 8 operand fragments for 16 MFMAs.
 //
-// Operands.  Both tiles go from global memory straight into LDS with global_load_lds_dwordx4,
-// in MFMA fragment order: fragment (32-row group g, 16-wide k step s) is 1 KiB, lane l's
-// 16 bytes being row g*32 + l%32, k = s*16 + (l/32)*8 .. +8, so every operand read is one
-// conflict-free ds_read_b128 and every DMA instruction reads 32-byte runs of 32 rows.  Two
+// Operands.  Both tiles go from global memory straight into LDS with global_load_lds_dwordx4:
+// one instruction moves 8 whole 128-byte row segments (64 k values of 8 rows), each 16-byte
+// chunk c of row r stored at position c ^ (r % 8), so the DMA reads whole cache lines and the
+// MFMA fragment reads (32 rows x one 16-byte chunk) are free of LDS bank conflicts.  Two
 // stages of 64 KiB alternate; one barrier per k step publishes a stage and frees the other.
 // The operand reads are written as inline ds_read_b128 with explicit lgkmcnt waits tied to
 // the fragment registers: the compiler cannot tell a DMA into one stage from reads of the
@@ -31,7 +31,6 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kGF = 8 * (kBK / 16);             // fragments per operand per stage (32)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -72,10 +71,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
                       const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                       void* __restrict__ out, int K, int N) {
-    __shared__ uint4 sA[2][kGF * 64];
-    __shared__ uint4 sW[2][kGF * 64];
-    const int task = blockIdx.x;
-    if (task >= *ntasks) return;
+    __shared__ uint4 sA[2][kBM * 8];             // 2 stages x 256 rows x 128 bytes
+    __shared__ uint4 sW[2][kBN * 8];
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so workgroup b
+    // runs on XCD b%8; each XCD takes one contiguous run of the (chunk-major) task list, so
+    // the tiles running together on an XCD share routed-row chunks and weight panels, and
+    // walk K in near lockstep, out of that XCD's L2.
+    const int nt = *ntasks;
+    const int per_xcd = (nt + 7) >> 3;
+    const int task = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || task >= nt) return;
     const int4 td = tasks[task];
     const int e = td.x, rb = td.y, rc = td.z, nb = td.w;
     const int lane = threadIdx.x & 63;
@@ -84,29 +89,37 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     const int j = lane & 31, h = lane >> 5;
     const int nk = K / kBK;
 
-    // weight row of n-group g (32 rows) for this lane
-    auto wrow = [&](int g) -> int {
+    // Operand tiles in LDS, per stage: [256 rows][128 bytes] for A and for W (the stage's 64
+    // k values of each row), the 16-byte chunk c of row r stored at position c ^ (r % 8).  A DMA
+    // instruction moves 8 whole 128-byte row segments (lane l: row l/8, position l%8, so
+    // global chunk (l%8) ^ (l/8)); every line it touches is read in full.  An MFMA fragment
+    // read (lane (j, h): row g*32 + j, chunk 2s + h) hits 8 distinct positions in every 8
+    // consecutive rows, so it is free of bank conflicts.
+    const int dl = lane >> 3;                   // row within a DMA instruction
+    const int dc = (lane & 7) ^ dl;             // global 16-byte chunk this lane moves
+    const uint16_t* srcA[8];
+    const uint16_t* srcW[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = wave * 64 + i * 8 + dl;   // tile row moved by this lane
+        srcA[i] = a + (size_t)(rb + min(r, rc - 1)) * K + dc * 8;
+        int wr;
         if (EPI == MOE_EPI_SWIGLU_BF16)
-            return g < 4 ? nb * 128 + g * 32 + j : N / 2 + nb * 128 + (g - 4) * 32 + j;
-        return nb * kBN + g * 32 + j;
-    };
-    // DMA sources: this wave moves row groups 2w and 2w+1 of both operands in every stage
-    const uint16_t* srcA0 = a + (size_t)(rb + min(2 * wave * 32 + j, rc - 1)) * K + h * 8;
-    const uint16_t* srcA1 = a + (size_t)(rb + min((2 * wave + 1) * 32 + j, rc - 1)) * K + h * 8;
-    const uint16_t* srcW0 = w + ((size_t)e * N + wrow(2 * wave)) * K + h * 8;
-    const uint16_t* srcW1 = w + ((size_t)e * N + wrow(2 * wave + 1)) * K + h * 8;
+            wr = r < 128 ? nb * 128 + r : N / 2 + nb * 128 + (r - 128);
+        else
+            wr = nb * kBN + r;
+        srcW[i] = w + ((size_t)e * N + wr) * K + dc * 8;
+    }
 
     auto issue = [&](int buf, int kt) {
         uint4* dA = sA[buf];
         uint4* dW = sW[buf];
         const int k0 = kt * kBK;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int f0 = (2 * wave) * 4 + s, f1 = (2 * wave + 1) * 4 + s;
-            __builtin_amdgcn_global_load_lds(srcA0 + k0 + s * 16, (lds_void*)(dA + f0 * 64), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(srcA1 + k0 + s * 16, (lds_void*)(dA + f1 * 64), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(srcW0 + k0 + s * 16, (lds_void*)(dW + f0 * 64), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(srcW1 + k0 + s * 16, (lds_void*)(dW + f1 * 64), 16, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+            const int row0 = wave * 64 + i * 8;
+            __builtin_amdgcn_global_load_lds(srcA[i] + k0, (lds_void*)(dA + row0 * 8), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(srcW[i] + k0, (lds_void*)(dW + row0 * 8), 16, 0, 0);
         }
     };
 
@@ -118,36 +131,35 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-    // LDS byte addresses of this lane's fragments: A row groups 4wm.., W groups of this wave
-    // ((4wn..) or, for SwiGLU, gate groups 2wn, 2wn+1 and up groups 4+2wn, 5+2wn)
-    const uint32_t lA = (uint32_t)(uintptr_t)(lds_void*)&sA[0][(4 * wm) * 4 * 64 + lane];
+    // Fragment read addresses, per 16-wide k step s: row j of a 32-row group, chunk 2s + h at
+    // its swizzled position; A groups 4wm.., W groups of this wave ((4wn..) or, for SwiGLU,
+    // gate groups 2wn, 2wn+1 and up groups 4+2wn, 5+2wn)
     const int wg0 = EPI == MOE_EPI_SWIGLU_BF16 ? 2 * wn : 4 * wn;
     const int wg2 = EPI == MOE_EPI_SWIGLU_BF16 ? 4 + 2 * wn : 4 * wn + 2;
-    const uint32_t lW0 = (uint32_t)(uintptr_t)(lds_void*)&sW[0][wg0 * 4 * 64 + lane];
-    const uint32_t lW2 = (uint32_t)(uintptr_t)(lds_void*)&sW[0][wg2 * 4 * 64 + lane];
-    constexpr uint32_t kStage = kGF * 64 * 16;  // bytes per stage buffer
-    constexpr int kG = 4 * 1024;                // bytes between row groups (4 k steps)
+    const uint32_t baseA = (uint32_t)(uintptr_t)(lds_void*)&sA[0][0];
+    const uint32_t baseW = (uint32_t)(uintptr_t)(lds_void*)&sW[0][0];
+    uint32_t pa[4], pw0[4], pw2[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const uint32_t in_row = (uint32_t)(j * 128 + (((2 * st + h) ^ (j & 7)) << 4));
+        pa[st] = baseA + (uint32_t)(4 * wm) * 4096u + in_row;
+        pw0[st] = baseW + (uint32_t)wg0 * 4096u + in_row;
+        pw2[st] = baseW + (uint32_t)wg2 * 4096u + in_row;
+    }
+    constexpr uint32_t kStage = 256 * 128;      // bytes per stage buffer
 
     auto compute = [&](uint32_t boff) {
-        const uint32_t pa = lA + boff, pw0 = lW0 + boff, pw2 = lW2 + boff;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            i32x4 fa0, fa1, fa2, fa3, fw0, fw1, fw2, fw3;
-            switch (s) {
-#define MOE_READS(S)                                                         \
-    case S:                                                                  \
-        fa0 = lds_read16<0 * kG + S * 1024>(pa);                             \
-        fa1 = lds_read16<1 * kG + S * 1024>(pa);                             \
-        fa2 = lds_read16<2 * kG + S * 1024>(pa);                             \
-        fa3 = lds_read16<3 * kG + S * 1024>(pa);                             \
-        fw0 = lds_read16<0 * kG + S * 1024>(pw0);                            \
-        fw1 = lds_read16<1 * kG + S * 1024>(pw0);                            \
-        fw2 = lds_read16<0 * kG + S * 1024>(pw2);                            \
-        fw3 = lds_read16<1 * kG + S * 1024>(pw2);                            \
-        break;
-                MOE_READS(0) MOE_READS(1) MOE_READS(2) MOE_READS(3)
-#undef MOE_READS
-            }
+        for (int st = 0; st < 4; ++st) {
+            const uint32_t qa = pa[st] + boff, qw0 = pw0[st] + boff, qw2 = pw2[st] + boff;
+            i32x4 fa0 = lds_read16<0 * 4096>(qa);
+            i32x4 fa1 = lds_read16<1 * 4096>(qa);
+            i32x4 fa2 = lds_read16<2 * 4096>(qa);
+            i32x4 fa3 = lds_read16<3 * 4096>(qa);
+            i32x4 fw0 = lds_read16<0>(qw0);
+            i32x4 fw1 = lds_read16<4096>(qw0);
+            i32x4 fw2 = lds_read16<0>(qw2);
+            i32x4 fw3 = lds_read16<4096>(qw2);
             lds_wait(fa0, fa1, fa2, fa3, fw0, fw1, fw2, fw3);
             const bf16x8 A[4] = {as_bf16x8(fa0), as_bf16x8(fa1), as_bf16x8(fa2), as_bf16x8(fa3)};
             const bf16x8 B[4] = {as_bf16x8(fw0), as_bf16x8(fw1), as_bf16x8(fw2), as_bf16x8(fw3)};
@@ -228,17 +240,18 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             int epilogue, void* out, hipStream_t s) {
     if (max_tasks <= 0) return hipSuccess;
     const int4* t = reinterpret_cast<const int4*>(tasks);
+    const int grid = (max_tasks + 7) / 8 * 8;    // whole rounds of the 8 XCDs
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_BF16>, dim3(max_tasks),
+            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_BF16>, dim3(grid),
                                dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
             break;
         case MOE_EPI_SWIGLU_BF16:
-            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_SWIGLU_BF16>, dim3(max_tasks),
+            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_SWIGLU_BF16>, dim3(grid),
                                dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
             break;
         default:
-            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_F32>, dim3(max_tasks),
+            hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_F32>, dim3(grid),
                                dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
     }
     return hipGetLastError();
