@@ -169,6 +169,60 @@ def bench_bf16_gemm(args, moe, synth, torch, np):
     print(json.dumps(result))
 
 
+def bench_ffn(args, moe, synth, torch, np):
+    """--workload ffn_mixtral_T<T>[_uniform]: the whole Mixtral-like expert FFN layer (E=8,
+    top-2, hidden 4096, FFN 1024, bf16), router logits skewed by -1.1 ln(e+1) unless
+    _uniform; --chunk-rows picks the task chunk (0 = 256)."""
+    parts = args.workload.split("_")
+    T = int(parts[2][1:])
+    skewed = not (len(parts) > 3 and parts[3] == "uniform")
+    E, k, H, F = 8, 2, 4096, 1024
+    d = synth.ffn_inputs(T, E, H, F, seed=0, skewed=skewed)
+    dev = torch.device("cuda:0")
+    tl = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    logits, x, wu, wd = tl(d["logits"]), tl(d["x"]), tl(d["w_up"]), tl(d["w_down"])
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    ws = torch.empty(moe.ffn_workspace_bytes(T, E, k, H, F), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        moe.ffn_forward(logits, x, wu, wd, k, synth.SOFTCAP, out, ws, chunk_rows=args.chunk_rows)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+    off = moe.ffn_workspace_offset(T, E, k, H, F, 2)
+    counts = ws[off:off + 4 * E].view(torch.int32).cpu().numpy()
+    rows = T * k
+    flops = 2.0 * rows * (2 * F * H + H * F)
+    tflops = flops / (us * 1e-6) / 1e12
+    result = {
+        "metric": "µs per Mixtral-like FFN layer + TFLOPS & %MFMA peak",
+        "value": round(us, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "E": E, "top_k": k, "hidden": H,
+                   "ffn": F, "chunk_rows": args.chunk_rows or 256, "skewed_router": skewed,
+                   "rows_per_expert_max_min": [int(counts.max()), int(counts.min())]},
+        "effective_tflops": round(tflops, 2),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "roofline": {"bound": "mfma", "kernel": "whole layer (gemm_bf16_kernel x2 + glue)",
+                     "achieved": round(tflops, 2), "peak": BF16_DENSE_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(us, 3)},
+    }
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -198,6 +252,9 @@ def main():
 
     if args.workload.startswith("bf16_grouped_gemm_"):
         bench_bf16_gemm(args, moe, synth, torch, np)
+        return
+    if args.workload.startswith("ffn_mixtral_"):
+        bench_ffn(args, moe, synth, torch, np)
         return
     d = synth.workload_inputs(args.workload)
     M, E, k, K, N, cap = d["M"], d["E"], d["k"], d["K"], d["N"], d["cap"]

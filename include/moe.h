@@ -117,6 +117,15 @@ int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_i
                           int32_t* route_slots, uint8_t* a_q, float* a_scales,
                           moe_stream_t stream);
 
+/* ---- [WEAVE] Mixtral-like layer: sort + gather of bf16 rows (no quantisation) ---------
+ * x bf16 [M][K] (K a multiple of 8).  Slots as in moe_quant_sort_gather: route r = t*k+j
+ * with a valid id takes slot = atomicAdd(cursors[e], 1); sorted_route_ids[slot] = r,
+ * route_slots[r] = slot (route_slots may be NULL; invalid ids get -1 and no row), and
+ * a[slot][:] = x[t][:] (bf16 [M*k][K]).  Rows inside a segment come in arrival order. */
+int moe_sort_gather_bf16(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
+                         int E, int32_t* cursors, int32_t* sorted_route_ids,
+                         int32_t* route_slots, uint16_t* a, moe_stream_t stream);
+
 /* ---- [FMF8] problem table (128x128 blockwise weights): weight preparation ---------------
  * w f32 [E][N][K] -> w_q E4M3 [E][N][K] and w_scales f32 [E][N/128][K/128], with the
  * activation rule above applied to every 128x128 block.  N, K multiples of 128. */
@@ -196,6 +205,25 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
+
+/* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------
+ * route (softcap, top-k) -> layout (chunk_rows rows per task, 0 = 256) -> bf16 sort+gather
+ * -> gated-up grouped GEMM with the SwiGLU epilogue -> down grouped GEMM (fp32 rows) ->
+ * routing-weighted combine:
+ *   act[r] = bf16(silu(x[t] . w_up[e][0:F]^T) * (x[t] . w_up[e][F:2F]^T)),
+ *   y[t] = bf16( sum_j w_tj * act[r_j] . w_down[e_j]^T )      (fp32 accumulation)
+ * logits f32 [M][E], x bf16 [M][H], w_up bf16 [E][2F][H] (gate rows then up rows),
+ * w_down bf16 [E][H][F] -> out bf16 [M][H].  H a multiple of 256, F of 128.  Workspace of
+ * moe_ffn_workspace_bytes(...) bytes; parts (for inspection): 0 topk_ids, 1 topk_weights,
+ * 2 counts, 3 offsets, 4 cursors, 5 up tasks, 6 down tasks, 7 ntasks, 8 sorted_route_ids,
+ * 9 route_slots, 10 gathered rows, 11 act, 12 down rows, 13 queue counters.  Seven plain
+ * launches on `stream`, no host synchronisation. */
+size_t moe_ffn_workspace_bytes(int M, int E, int k, int H, int F);
+int64_t moe_ffn_workspace_offset(int M, int E, int k, int H, int F, int which);
+int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up,
+                    const uint16_t* w_down, int M, int E, int k, int H, int F, float softcap,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
+                    moe_stream_t stream);
 
 #ifdef __cplusplus
 }

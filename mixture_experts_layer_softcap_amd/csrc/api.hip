@@ -217,6 +217,45 @@ int forward_graph(const FwdArgs& a, hipStream_t s) {
 
 const DeviceInfo& device_info() { return g_dev[t_dev].info; }
 
+// ---- Mixtral-like expert FFN layer (BF16) ---------------------------------------------
+constexpr int kFfnParts = 14;
+struct FfnLayout {
+    size_t off[kFfnParts];
+    size_t total;
+};
+bool ffn_dims_ok(int M, int E, int k, int H, int F) {
+    return M >= 1 && route_dims_ok(M, E, k) && H >= 256 && H % 256 == 0 && F >= 128 &&
+           F % 128 == 0 && (long long)M * k * (long long)(H > F ? H : F) < (1LL << 40);
+}
+FfnLayout ffn_layout(int M, int E, int k, int H, int F) {
+    const size_t R = (size_t)M * k;
+    const size_t tu = (size_t)max_tasks_ll(M, k, E, 2 * F / 256, 1);
+    const size_t td = (size_t)max_tasks_ll(M, k, E, H / 256, 1);
+    const size_t sz[kFfnParts] = {
+        R * 4,                     // 0 topk_ids
+        R * 4,                     // 1 topk_weights
+        (size_t)E * 4,             // 2 counts
+        (size_t)(E + 1) * 4,       // 3 offsets
+        (size_t)E * 4,             // 4 cursors
+        tu * sizeof(moe_task),     // 5 tasks of the gated-up GEMM
+        td * sizeof(moe_task),     // 6 tasks of the down GEMM
+        16,                        // 7 ntasks (up, down) and two queue pairs
+        R * 4,                     // 8 sorted_route_ids
+        R * 4,                     // 9 route_slots
+        R * (size_t)H * 2,         // 10 gathered rows, bf16 [R][H]
+        R * (size_t)F * 2,         // 11 act = silu(gate) * up, bf16 [R][F]
+        R * (size_t)H * 4,         // 12 down-projection rows, f32 [R][H]
+        16,                        // 13 queue counters
+    };
+    FfnLayout L;
+    size_t p = 0;
+    for (int i = 0; i < kFfnParts; ++i) {
+        L.off[i] = p;
+        p = align256(p + sz[i]);
+    }
+    L.total = p;
+    return L;
+}
 }  // namespace moe
 
 using namespace moe;
@@ -282,6 +321,17 @@ int moe_quant_sort_gather(const uint16_t* x, int M, int K, const int32_t* topk_i
     if (rc) return rc;
     return hip_status(launch_qsg(x, M, K, topk_ids, k, E, cursors, sorted_route_ids,
                                  route_slots, a_q, a_scales, (hipStream_t)stream));
+}
+
+int moe_sort_gather_bf16(const uint16_t* x, int M, int K, const int32_t* topk_ids, int k,
+                         int E, int32_t* cursors, int32_t* sorted_route_ids,
+                         int32_t* route_slots, uint16_t* a, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || K < 8 || K % 8) return MOE_E_INVAL;
+    if (M > 0 && (!x || !topk_ids || !cursors || !sorted_route_ids || !a)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_gather_bf16(x, M, K, topk_ids, k, E, cursors, sorted_route_ids,
+                                         route_slots, a, (hipStream_t)stream));
 }
 
 int moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q, float* w_scales,
@@ -388,6 +438,67 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
                 uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
     return moe_forward_ex(logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
                           workspace_bytes, 0, 0, stream);
+}
+
+// ---- Mixtral-like expert FFN layer (BF16) ---------------------------------------------
+size_t moe_ffn_workspace_bytes(int M, int E, int k, int H, int F) {
+    if (!ffn_dims_ok(M, E, k, H, F)) return 0;
+    return ffn_layout(M, E, k, H, F).total;
+}
+
+int64_t moe_ffn_workspace_offset(int M, int E, int k, int H, int F, int which) {
+    if (!ffn_dims_ok(M, E, k, H, F) || which < 0 || which >= kFfnParts) return -1;
+    return (int64_t)ffn_layout(M, E, k, H, F).off[which];
+}
+
+int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up,
+                    const uint16_t* w_down, int M, int E, int k, int H, int F, float softcap,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
+                    moe_stream_t stream) {
+    if (!ffn_dims_ok(M, E, k, H, F)) return MOE_E_INVAL;
+    if (!logits || !x || !w_up || !w_down || !out || !workspace) return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    if (chunk_rows < 0 || chunk_rows > 256) return MOE_E_INVAL;
+    const FfnLayout L = ffn_layout(M, E, k, H, F);
+    if (workspace_bytes < L.total) return MOE_E_NOSPC;
+    int rc = check_device();
+    if (rc) return rc;
+    const int chunk = chunk_rows ? chunk_rows : 256;
+    char* base = static_cast<char*>(workspace);
+    auto at = [&](int i) { return base + L.off[i]; };
+    int32_t* ids = reinterpret_cast<int32_t*>(at(0));
+    float* wts = reinterpret_cast<float*>(at(1));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(2));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(3));
+    int32_t* cursors = reinterpret_cast<int32_t*>(at(4));
+    moe_task* tu = reinterpret_cast<moe_task*>(at(5));
+    moe_task* td = reinterpret_cast<moe_task*>(at(6));
+    int32_t* nt = reinterpret_cast<int32_t*>(at(7));
+    int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
+    int32_t* slots = reinterpret_cast<int32_t*>(at(9));
+    uint16_t* rows = reinterpret_cast<uint16_t*>(at(10));
+    uint16_t* act = reinterpret_cast<uint16_t*>(at(11));
+    float* down = reinterpret_cast<float*>(at(12));
+    uint32_t* queue = reinterpret_cast<uint32_t*>(at(13));
+    const int nbu = 2 * F / 256, nbd = H / 256;
+    const int mtu = (int)max_tasks_ll(M, k, E, nbu, chunk);
+    const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
+        (e = launch_layout(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu, mtu, nt,
+                           queue, s)) != hipSuccess ||
+        (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
+                           nt + 1, queue + 2, s)) != hipSuccess ||
+        (e = launch_gather_bf16(x, M, H, ids, k, E, cursors, sorted, slots, rows, s)) !=
+            hipSuccess ||
+        (e = launch_gemm_bf16(rows, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s)) !=
+            hipSuccess ||
+        (e = launch_gemm_bf16(act, F, w_down, H, td, nt + 1, mtd, MOE_EPI_STORE_F32, down, s)) !=
+            hipSuccess ||
+        (e = launch_scatter(down, slots, wts, ids, M, k, E, H, out, s)) != hipSuccess)
+        return hip_status(e);
+    return MOE_OK;
 }
 
 }  // extern "C"

@@ -26,6 +26,11 @@ hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k
                       int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,
                       uint8_t* a_q, float* a_scales, hipStream_t s);
 
+// bf16 sort/gather (K a multiple of 8)
+hipError_t launch_gather_bf16(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
+                              int32_t* cursors, int32_t* sorted_route_ids,
+                              int32_t* route_slots, uint16_t* a, hipStream_t s);
+
 hipError_t launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* w_q,
                                    float* w_scales, hipStream_t s);
 

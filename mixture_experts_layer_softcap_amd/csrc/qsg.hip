@@ -91,7 +91,48 @@ __global__ __launch_bounds__(kThreads) void qsg_kernel(
     }
 }
 
+// The bf16 form of the same sort/gather ([WEAVE] Mixtral-like layer: rows are gathered into
+// expert-contiguous order without quantisation): slots as above, then every thread copies
+// its 16 bytes of the token's row to each of the k sorted rows.
+__global__ __launch_bounds__(kThreads) void gather_bf16_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ ids, int k, int E,
+    int32_t* __restrict__ cursors, int32_t* __restrict__ sorted_route_ids,
+    int32_t* __restrict__ route_slots, uint16_t* __restrict__ a) {
+    __shared__ int s_slot[64];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* xrow = x + (size_t)t * K;
+    if (tid < k) {
+        const int r = t * k + tid;
+        const int e = ids[r];
+        int slot = -1;
+        if ((unsigned)e < (unsigned)E) {
+            slot = atomicAdd(&cursors[e], 1);
+            sorted_route_ids[slot] = r;
+        }
+        s_slot[tid] = slot;
+        if (route_slots) route_slots[r] = slot;
+    }
+    __syncthreads();
+    for (int k0 = tid * 8; k0 < K; k0 += kSpan) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xrow + k0);
+        for (int j = 0; j < k; ++j) {
+            const int slot = s_slot[j];
+            if (slot >= 0) *reinterpret_cast<uint4*>(a + (size_t)slot * K + k0) = raw;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather_bf16(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
+                              int32_t* cursors, int32_t* sorted_route_ids,
+                              int32_t* route_slots, uint16_t* a, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_bf16_kernel, dim3(M), dim3(kThreads), 0, s, x, M, K, ids, k, E,
+                       cursors, sorted_route_ids, route_slots, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
                       int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,

@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_max_tasks": (_I, [_I, _I, _I, _I, _I]),
     "moe_build_layout": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
     "moe_quant_sort_gather": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_sort_gather_bf16": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_gemm_n_tile": (_I, [_I]),
     "moe_grouped_gemm": (_I, [_I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I,
@@ -48,6 +49,9 @@ SIGNATURES = {
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _I, _P]),
+    "moe_ffn_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "moe_ffn_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
+    "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _P]),
 }
 
 _lib = None
@@ -176,3 +180,32 @@ def forward(logits, x, w_q, w_scales, k: int, softcap: float, out, workspace,
     _call("moe_forward_ex", _ptr(logits), _ptr(x), _ptr(w_q), _ptr(w_scales), M, E, k, K, N,
           softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
           chunk_rows, flags, _stream(stream))
+
+
+def sort_gather_bf16(x, topk_ids, E: int, cursors, sorted_route_ids, a, route_slots=None,
+                     stream=None):
+    M, K = x.shape
+    k = topk_ids.shape[1]
+    _call("moe_sort_gather_bf16", _ptr(x), M, K, _ptr(topk_ids), k, E, _ptr(cursors),
+          _ptr(sorted_route_ids), _ptr(route_slots), _ptr(a), _stream(stream))
+
+
+def ffn_workspace_bytes(M: int, E: int, k: int, H: int, F: int) -> int:
+    v = lib().moe_ffn_workspace_bytes(M, E, k, H, F)
+    if v == 0:
+        raise MoeError("moe_ffn_workspace_bytes", MOE_E_INVAL)
+    return v
+
+
+def ffn_workspace_offset(M: int, E: int, k: int, H: int, F: int, which: int) -> int:
+    return lib().moe_ffn_workspace_offset(M, E, k, H, F, which)
+
+
+def ffn_forward(logits, x, w_up, w_down, k: int, softcap: float, out, workspace,
+                chunk_rows: int = 0, stream=None):
+    M, E = logits.shape
+    H = x.shape[1]
+    F = w_down.shape[2]
+    _call("moe_ffn_forward", _ptr(logits), _ptr(x), _ptr(w_up), _ptr(w_down), M, E, k, H, F,
+          softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          chunk_rows, _stream(stream))

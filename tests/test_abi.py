@@ -61,6 +61,12 @@ def test_workspace_queries(L):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < b
     assert L.moe_forward_workspace_bytes(128, 256, 8, 2000, 512) == 0   # K % 128
     assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 13) == -1
+    fo = [L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, i) for i in range(14)]
+    assert fo == sorted(fo) and all(o % 256 == 0 for o in fo)
+    assert fo[-1] < L.moe_ffn_workspace_bytes(64, 8, 2, 512, 256)
+    assert L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, 14) == -1
+    assert L.moe_gemm_n_tile(0) == 128 and L.moe_gemm_n_tile(1) == 256
+    assert L.moe_gemm_n_tile(5) == -1
 
 
 NULL = None
@@ -97,6 +103,18 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 65, 0, S) == INVAL    # chunk
     assert f(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 0, S) == INVAL
     assert L.moe_forward(P, P, P, P, 0, 16, 2, 256, 256, 30.0, P, P, ws, S) == INVAL
+    assert L.moe_sort_gather_bf16(P, 4, 100, P, 2, 8, P, P, P, P, S) == INVAL   # K % 8
+    assert gg(1, P, P, 4, 96, P, P, 2, 256, P, P, 8, 256, P, 1, P, P, S) == INVAL  # K % 64
+    assert gg(1, P, P, 4, 128, P, P, 2, 384, P, P, 8, 256, P, 1, P, P, S) == INVAL  # N % 256
+    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 257, P, 1, P, P, S) == INVAL  # chunk
+    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 256, P, 2, P, P, S) == INVAL  # ROUTE_F32
+    fw = L.moe_ffn_workspace_bytes(16, 8, 2, 512, 256)
+    assert fw > 0 and L.moe_ffn_workspace_bytes(16, 8, 2, 500, 256) == 0         # H % 256
+    assert L.moe_ffn_workspace_bytes(16, 8, 2, 512, 200) == 0                    # F % 128
+    ff = L.moe_ffn_forward
+    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw - 1, 0, S) == NOSPC
+    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 300, S) == INVAL   # chunk
+    assert ff(P, NULL, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 0, S) == INVAL
 
 
 def test_no_gpu_gives_a_device_status():

@@ -137,3 +137,57 @@ def test_bf16_gemm_full_up_projection_sampled():
     rl = np.array(sorted(pick), np.int32)
     _, ref = orc.gemm_bf16(d["A"], d["W"], off, rows_list=rl)
     assert_f32_close(y[rl], ref, "up projection sample")
+
+
+# ---- the Mixtral-like expert FFN layer ------------------------------------------------
+
+def test_sort_gather_bf16_copies_rows_into_segments():
+    T, E, k, H = 333, 8, 2, 512
+    d = synth.ffn_inputs(T, E, H, 256, seed=4, weights=False)
+    ids, _ = orc.route(d["logits"], k, 30.0)
+    counts, offsets = orc.layout(ids, E)
+    R = T * k
+    cur = to_dev(offsets[:E].copy())
+    srt, slots = zeros((R,), torch.int32), zeros((R,), torch.int32)
+    a = zeros((R, H), torch.int16)
+    moe.sort_gather_bf16(to_dev(d["x"]), to_dev(ids), E, cur, srt, a, route_slots=slots)
+    torch.cuda.synchronize()
+    srt, slots, a = to_np(srt), to_np(slots), to_np(a, np.uint16)
+    np.testing.assert_array_equal(to_np(cur), offsets[1:])
+    r = np.arange(R)
+    np.testing.assert_array_equal(srt[slots], r)                  # slots are a permutation
+    np.testing.assert_array_equal(a[slots], d["x"][r // k])      # rows copied bit for bit
+    for e in range(E):                                            # segment membership
+        seg = np.sort(srt[offsets[e]:offsets[e + 1]])
+        np.testing.assert_array_equal(seg, np.flatnonzero(ids.reshape(-1) == e))
+
+
+def run_ffn(d, k, chunk=0):
+    logits, x, wu, wd = d["logits"], d["x"], d["w_up"], d["w_down"]
+    T, E = logits.shape
+    H, F = x.shape[1], wd.shape[2]
+    ws = torch.empty(moe.ffn_workspace_bytes(T, E, k, H, F), dtype=torch.uint8, device="cuda")
+    out = zeros((T, H), torch.int16)
+    moe.ffn_forward(to_dev(logits), to_dev(x), to_dev(wu), to_dev(wd), k, 30.0, out, ws,
+                    chunk_rows=chunk)
+    torch.cuda.synchronize()
+    return to_np(out, np.uint16)
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_ffn_layer_small_full(chunk):
+    T, E, k, H, F = 300, 8, 2, 512, 256
+    d = synth.ffn_inputs(T, E, H, F, seed=7)
+    y = run_ffn(d, k, chunk)
+    _, ref = orc.ffn_tokens(d["logits"], d["x"], d["w_up"], d["w_down"], k, 30.0)
+    assert_bf16_close(y, ref, f"ffn chunk={chunk}")
+
+
+def test_ffn_layer_mixtral_shape_sampled():
+    # T=8192 tokens, E=8, top-2, hidden 4096, FFN 1024, skewed router (-1.1 ln(e+1) bias)
+    T, E, k, H, F = 8192, 8, 2, 4096, 1024
+    d = synth.ffn_inputs(T, E, H, F, seed=0)
+    y = run_ffn(d, k)
+    tok = np.random.default_rng(1).choice(T, 48, replace=False).astype(np.int32)
+    _, ref = orc.ffn_tokens(d["logits"], d["x"], d["w_up"], d["w_down"], k, 30.0, tokens=tok)
+    assert_bf16_close(y[tok], ref, "ffn sample")
