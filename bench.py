@@ -33,6 +33,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="fused_fp8_M128_E256_k8_K2048_N512")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--staged", action="store_true",
+                   help="run the five staged kernels even where the fused small-batch path "
+                        "(route, fused GEMM, combine) applies")
     p.add_argument("--static-grid", action="store_true",
                    help="walk the task list with a fixed stride instead of the atomic queue")
     p.add_argument("--chunk-rows", type=int, default=0)
@@ -44,17 +47,17 @@ def parse():
     return p.parse_args()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kernel):
     """HBM bytes per launch of the timed grouped GEMM from the committed rocprofv3 counter
-    record (FETCH_SIZE + WRITE_SIZE, copy-calibrated) for this workload, or None when there is
-    none or the kernel's source has changed since the counters were taken."""
+    record (FETCH_SIZE + WRITE_SIZE, copy-calibrated) for this workload and kernel, or None
+    when there is none or the kernel's source has changed since the counters were taken."""
     import glob
     import hashlib
 
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.json"))):
         with open(path) as f:
             rec = json.load(f)
-        if rec.get("workload") != workload:
+        if rec.get("workload") != workload or not rec.get("kernel", "").startswith(kernel):
             continue
         src = os.path.join(ROOT, rec["source"])
         if not os.path.exists(src):
@@ -65,14 +68,16 @@ def measured_traffic(workload):
     return None
 
 
-def gemm_algorithmic_bytes(counts, M, k, K, N):
+def gemm_algorithmic_bytes(counts, M, k, K, N, fused=False):
     """Bytes the grouped GEMM must move: each non-empty expert's FP8 weights and scales once,
-    the routed FP8 rows and their scales once, the fp32 routed output rows once."""
+    the fp32 routed output rows once, and its inputs once: the routed FP8 rows, their scales
+    and sorted ids (staged), or the bf16 token rows and the routed ids (fused: layout, gather
+    and quantisation inside the GEMM)."""
     nonempty = int((counts > 0).sum())
     R = M * k
     Nb, Kb = N // 128, K // 128
     weights = nonempty * (N * K + Nb * Kb * 4)
-    acts = R * K + Kb * R * 4 + R * 4
+    acts = M * K * 2 + R * 4 if fused else R * K + Kb * R * 4 + R * 4
     out = R * N * 4
     return weights + acts + out
 
@@ -223,6 +228,25 @@ def bench_ffn(args, moe, synth, torch, np):
     print(json.dumps(result))
 
 
+def staged_gemm(args, moe, torch, wsp, M, E, k, K, N, chunk, wqs, wss, copies, rows_out):
+    """The staged step's grouped GEMM alone (ROUTE_F32 epilogue) on the task list, FP8 rows and
+    scales the last staged forward left in the workspace."""
+    R = M * k
+    a_q = wsp(9, torch.uint8, R * K).view(R, K)
+    a_s = wsp(10, torch.float32, (K // 128) * R)
+    max_tasks = moe.max_tasks(M, k, E, N // 128, chunk)
+    tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
+    ntasks = wsp(6, torch.int32, 1)
+    queue = None if args.static_grid else wsp(7, torch.int32, 2)
+    sorted_ids = wsp(8, torch.int32, R)
+
+    def gemm(i):
+        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, wqs[i % copies], wss[i % copies],
+                         tasks, ntasks, chunk, rows_out, moe.MOE_EPI_ROUTE_F32, queue=queue,
+                         sorted_route_ids=sorted_ids)
+    return gemm
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -273,7 +297,7 @@ def main():
     out = torch.empty((M, N), dtype=torch.int16, device=dev)
     ws = torch.empty(moe.forward_workspace_bytes(M, E, k, K, N), dtype=torch.uint8, device=dev)
     flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
-        (moe.MOE_FWD_GRAPH if args.graph else 0)
+        (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -296,9 +320,10 @@ def main():
     total_ms = evs[0].elapsed_time(evs[-1])
     us_layer = total_ms * 1e3 / args.steps
 
-    # routing statistics of this input (read back from the workspace, outside timing)
-    off = moe.forward_workspace_offset(M, E, k, K, N, 2)
-    counts = ws[off:off + 4 * E].view(torch.int32).cpu().numpy()
+    # routing statistics of this input (its routed ids read back, outside timing)
+    off = moe.forward_workspace_offset(M, E, k, K, N, 0)
+    ids_np = ws[off:off + 4 * M * k].view(torch.int32).cpu().numpy()
+    counts = np.bincount(ids_np[(ids_np >= 0) & (ids_np < E)], minlength=E)
 
     # ---- dominant kernel alone: the grouped GEMM, same launch configuration ------------
     def wsp(i, dtype, n):
@@ -307,21 +332,21 @@ def main():
 
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (32 if -(-R // E) <= 48 else 64))
-    a_q = wsp(9, torch.uint8, R * K).view(R, K)
-    a_s = wsp(10, torch.float32, (K // 128) * R)
-    max_tasks = moe.max_tasks(M, k, E, N // 128, chunk)
-    tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
-    ntasks = wsp(6, torch.int32, 1)
-    queue = None if args.static_grid else wsp(7, torch.int32, 2)
-    sorted_ids = wsp(8, torch.int32, R)
+    fused = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags) == 3
     rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
-    # the workspace still holds the layout of the last forward, built with the same chunk
+    if fused:
+        # the step's GEMM reads the routed ids (workspace part 0, written by its route stage)
+        ids_ws = wsp(0, torch.int32, R).view(M, k)
 
-    def gemm(i):
-        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, wqs[i % copies], wss[i % copies],
-                         tasks, ntasks, chunk, rows_out, moe.MOE_EPI_ROUTE_F32, queue=queue,
-                         sorted_route_ids=sorted_ids)
-
+        def gemm(i):
+            moe.grouped_gemm_routed(x, ids_ws, E, wqs[i % copies], wss[i % copies], rows_out)
+    else:
+        # one staged step writes the task list, FP8 rows, scales and sorted ids it times
+        moe.forward(logits, x, wqs[0], wss[0], k, cap, out, ws, chunk_rows=args.chunk_rows,
+                    flags=flags | moe.MOE_FWD_STAGED)
+        torch.cuda.synchronize()
+        gemm = staged_gemm(args, moe, torch, wsp, M, E, k, K, N, chunk, wqs, wss, copies,
+                           rows_out)
     for i in range(copies * 2):
         gemm(i)
     torch.cuda.synchronize()
@@ -332,9 +357,15 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     gemm_us = g0.elapsed_time(g1) * 1e3 / args.steps
-    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N)
+    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N, fused)
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
 
+    if fused:
+        gemm_kernel = "gemm_fp8_fused_kernel (grouped FP8 GEMM from routed ids, rows at route ids)"
+    elif K == 2048 and chunk <= 16:
+        gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
+    else:
+        gemm_kernel = "gemm_fp8_kernel (grouped FP8 GEMM, ROUTE_F32)"
     lbytes = layer_algorithmic_bytes(counts, M, E, k, K, N)
     flops = 2.0 * M * k * N * K
     result = {
@@ -352,7 +383,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
-                   "gemm_task_walk": ("contiguous ranges, per-wave pull" if K == 2048 and chunk <= 16
+                   "path": ("3 kernels: route, grouped GEMM from the routed ids, combine" if fused
+                            else "5 kernels: route, layout, QSG, grouped GEMM, combine"),
+                   "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
+                                      else "contiguous ranges, per-wave pull"
+                                      if K == 2048 and chunk <= 16
                                       else "static stride" if args.static_grid else "atomic queue"),
                    "launch": "graph" if args.graph else "plain",
                    "chunk_rows": chunk},
@@ -362,12 +397,10 @@ def main():
         "layer_algorithmic_bytes": lbytes,
         "nonempty_experts": int((counts > 0).sum()),
         "roofline": {"bound": "hbm",
-                     "kernel": ("gemm_fp8_range_kernel" if K == 2048 and chunk <= 16
-                                else "gemm_fp8_kernel") + " (grouped FP8 GEMM, ROUTE_F32)",
+                     "kernel": gemm_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload)
-                     if K == 2048 and chunk <= 16 else None,
+                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" ")[0]),
                      "algorithmic_bytes_per_launch": gbytes,
                      "avg_launch_us": round(gemm_us, 3)},
     }

@@ -167,6 +167,22 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                      int chunk_rows, uint32_t* queue, int epilogue,
                      const int32_t* sorted_route_ids, void* out, moe_stream_t stream);
 
+/* ---- [FMF8] Baseline items 2-6 fused: grouped FP8 GEMM straight from routed ids ------------
+ * The small-batch GEMM of moe_forward: K = 2048, M*k <= 2048, N a multiple of 128, and E at
+ * most about three times the CU count (one CU's share of the E*N/16 weight slices may touch at
+ * most four experts).  The weights are split evenly over one workgroup per CU, independent of
+ * the routing; each workgroup finds its experts' routes in topk_ids [M][k] (ascending route
+ * id), quantises those rows of x bf16 [M][K] with the moe_quant_sort_gather rule straight into
+ * its MFMA tiles, and streams each of its weight slices once per 64 routed rows of the expert.
+ * Writes rows f32 [M*k][N] at route ids (rows[t*k+j] = the GEMM row of route (t, j); rows of
+ * invalid ids are not written).  counts [E] and offsets [E+1] are optional (both NULL or
+ * both set): when set, a second small kernel writes them as moe_build_layout would.
+ * w_q / w_scales as for moe_grouped_gemm.  MOE_E_INVAL outside the limits above. */
+int moe_grouped_gemm_routed(const uint16_t* x, const int32_t* topk_ids, int M, int k, int E,
+                            int K, const uint8_t* w_q, const float* w_scales, int N,
+                            float* rows, int32_t* counts, int32_t* offsets,
+                            moe_stream_t stream);
+
 /* ---- [FMF8] Baseline item 7 (scatter, routing-weighted) ---------------------------------
  * rows f32 [M*k][N] are the GEMM rows.  Route r = t*k+j reads row route_slots[r] (rows in
  * sorted order, MOE_EPI_STORE_F32 + the slots recorded by moe_quant_sort_gather), or row r
@@ -183,7 +199,7 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
 
 /* Byte offset inside the workspace of one intermediate, for inspection in tests:
  * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
- * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (sorted order), 12 route_slots.
+ * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (at route ids), 12 route_slots.
  * -1 on bad arguments. */
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
 
@@ -201,10 +217,20 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  * walk instead of the atomic queue (grouped GEMM forms that walk a queue). */
 #define MOE_FWD_GRAPH 1
 #define MOE_FWD_STATIC_GRID 2
+/* bit 2: always run the five staged kernels.  Without it, a small batch (the limits of
+ * moe_grouped_gemm_routed, chunk_rows 16) runs three: route, the grouped GEMM straight from
+ * the routed ids (layout, sort/gather and quantisation inside it; fp32 rows at route ids),
+ * and the combine; the workspace then holds topk_ids, topk_weights and the GEMM rows (parts
+ * 0, 1 and 11) but no counts, offsets, task list, sorted ids, a_q, a_scales or slots. */
+#define MOE_FWD_STAGED 4
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
+
+/* Number of kernels moe_forward_ex launches for these arguments: 3 (the small-batch path of
+ * bit 2's description) or 5 (staged); MOE_E_INVAL for arguments moe_forward_ex rejects. */
+int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
 /* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------
  * route (softcap, top-k) -> layout (chunk_rows rows per task, 0 = 256) -> bf16 sort+gather

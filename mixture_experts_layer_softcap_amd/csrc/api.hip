@@ -149,6 +149,14 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     const int max_tasks = (int)max_tasks_ll(a.M, a.k, a.E, Nb, a.chunk);
     hipError_t e;
     if ((e = launch_route(a.logits, a.M, a.E, a.k, a.softcap, ids, wts, s)) != hipSuccess) return e;
+    if (!(a.flags & MOE_FWD_STAGED) && forward_fused_applies(a.M, a.k, a.E, a.K, a.N, a.chunk)) {
+        // small batch: layout, sort/gather and quantisation run inside the GEMM, whose fp32
+        // rows land at their route ids
+        if ((e = launch_gemm_fp8_fused(a.x, ids, a.M, a.k, a.E, a.w_q, a.w_scales, a.N, rows,
+                                       s)) != hipSuccess)
+            return e;
+        return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+    }
     if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
                            max_tasks, ntasks, queue, s)) != hipSuccess)
         return e;
@@ -156,11 +164,12 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         hipSuccess)
         return e;
     uint32_t* q = (a.flags & MOE_FWD_STATIC_GRID) ? nullptr : queue;
+    // fp32 rows at their route ids: the combine reads a token's k rows without a slot table
     if ((e = launch_gemm_fp8(a_q, a_s, a.M * a.k, a.K, a.w_q, a.w_scales, a.E, a.N, tasks,
-                             ntasks, max_tasks, a.chunk, q, MOE_EPI_STORE_F32, nullptr, rows,
+                             ntasks, max_tasks, a.chunk, q, MOE_EPI_ROUTE_F32, sorted, rows,
                              s)) != hipSuccess)
         return e;
-    return launch_scatter(rows, slots, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+    return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
 }
 
 // graph cache: one executable graph per (device, arguments)
@@ -387,6 +396,22 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                                       sorted_route_ids, out, (hipStream_t)stream));
 }
 
+int moe_grouped_gemm_routed(const uint16_t* x, const int32_t* topk_ids, int M, int k, int E,
+                            int K, const uint8_t* w_q, const float* w_scales, int N,
+                            float* rows, int32_t* counts, int32_t* offsets,
+                            moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || M < 1 || N < 128 || N % 128) return MOE_E_INVAL;
+    if (!x || !topk_ids || !w_q || !w_scales || !rows || (!counts != !offsets))
+        return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    if (!forward_fused_applies(M, k, E, K, N, 16)) return MOE_E_INVAL;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_gemm_fp8_fused(x, topk_ids, M, k, E, w_q, w_scales, N, rows, s);
+    if (e == hipSuccess && counts) e = launch_counts(topk_ids, M, k, E, counts, offsets, s);
+    return hip_status(e);
+}
+
 int moe_scatter(const float* rows, const int32_t* route_slots, const float* topk_weights,
                 const int32_t* topk_ids, int M, int k, int E, int N, uint16_t* out,
                 moe_stream_t stream) {
@@ -416,7 +441,7 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     if (!logits || !x || !w_q || !w_scales || !out || !workspace) return MOE_E_INVAL;
     if (softcap != softcap) return MOE_E_INVAL;
     if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
-    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID)) return MOE_E_INVAL;
+    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
     if (workspace_bytes < ws_layout(M, E, k, K, N).total) return MOE_E_NOSPC;
     int rc = check_device();
     if (rc) return rc;
@@ -431,6 +456,16 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     if (!(flags & MOE_FWD_GRAPH) || cs != hipStreamCaptureStatusNone)
         return hip_status(enqueue_forward(a, s));
     return forward_graph(a, s);
+}
+
+int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags) {
+    if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
+    if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
+    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E);
+    return !(flags & MOE_FWD_STAGED) && forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
 
 int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,

@@ -57,13 +57,6 @@ __device__ __forceinline__ TaskD load_task(const int4* __restrict__ tasks, int i
     return {t.x, t.y, t.z, t.w};
 }
 
-__device__ __forceinline__ v8i pack8(uint4 lo, uint4 hi) {
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
-}
-
 // position of the n-th (0-based) set bit of m; m has more than n set bits
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
     for (int i = 0; i < n; ++i) m &= m - 1;
@@ -107,30 +100,6 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ a,
     }
 }
 
-
-// Workgroup barrier that leaves the newest VM vector-memory operations of each wave in flight.
-// Every LDS operation has completed (lgkmcnt 0) and every LDS DMA older than those VM loads
-// has landed (DMA counts in vmcnt and decrements once its data is in LDS), so what was written
-// to LDS before it is visible after it.  The compiler's own barrier would drain vmcnt to zero
-// and with it the weight stream; the signal fences only keep the compiler from moving memory
-// operations across the barrier.
-template <int VM>
-__device__ __forceinline__ void barrier_keep_vm() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt is six bits");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v8i pack8v(u32x4 lo, u32x4 hi) {
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
-}
 
 // NT: weights are read with the non-temporal hint (streamed once, kept out of the caches).
 template <int KB2, int EPI, bool NT>

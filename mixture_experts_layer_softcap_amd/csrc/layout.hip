@@ -105,6 +105,30 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
     }
 }
 
+// Per-expert counts and exclusive offsets alone (the layout kernel without the task list).
+__global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restrict__ ids, int R,
+                                                          int E, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets) {
+    __shared__ int s_cnt[kThreads];
+    __shared__ int s_wsum[kWaves + 1];
+    const int tid = threadIdx.x;
+    s_cnt[tid] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += kThreads) {
+        const int e = ids[r];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    const int c = tid < E ? s_cnt[tid] : 0;
+    int total;
+    const int o = block_exclusive_scan(c, s_wsum, total);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = o;
+        if (tid == E - 1) offsets[E] = o + c;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
@@ -113,6 +137,13 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
     (void)max_tasks;  // capacity checked on the host against moe_max_tasks
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
                        chunk_rows, counts, offsets, cursors, tasks, ntasks, queue);
+    return hipGetLastError();
+}
+
+hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* counts,
+                         int32_t* offsets, hipStream_t s) {
+    hipLaunchKernelGGL(counts_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, counts,
+                       offsets);
     return hipGetLastError();
 }
 

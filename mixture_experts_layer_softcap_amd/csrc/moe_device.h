@@ -29,19 +29,26 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     const uint32_t u = __float_as_uint(y);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;
-    if (a >= 0x43E00000u) return sign | 0x7Eu;            // 448.0f
-    if (a < 0x3C800000u) {                                 // 2^-6: subnormal grid
-        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scale, RNE
-        return sign | (uint32_t)q;                         // 0..8 (8 = smallest normal)
-    }
-    uint32_t e = (a >> 23) - 120u;                         // biased E4M3 exponent, 1..15
-    uint32_t m = a & 0x7FFFFFu;
-    uint32_t keep = m >> 20;                               // 3 mantissa bits
-    const uint32_t rest = m & 0xFFFFFu;                    // 20 dropped bits
-    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
-    if (keep == 8u) { keep = 0u; ++e; }
-    return sign | (e << 3) | keep;
+    // normal range [2^-6, 448): keep 3 of the 23 mantissa bits, round to nearest even by
+    // adding 0x7FFFF plus the lowest kept bit (a carry out of the mantissa bumps the exponent),
+    // then rebias the exponent from 127 to 7 (120 << 3 in the code's units)
+    const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    // below 2^-6: the subnormal grid m * 2^-9, m = RNE(|y| * 512) in 0..8 (exact scaling)
+    const uint32_t sub =
+        (uint32_t)__builtin_rintf(__uint_as_float(a < 0x3C800000u ? a : 0u) * 512.0f);
+    uint32_t code = a < 0x3C800000u ? sub : normal;
+    code = a >= 0x43E00000u ? 0x7Eu : code;               // |y| >= 448 saturates
+    return a > 0x7F800000u ? 0x7Fu : (sign | code);       // NaN
+}
+
+// Router selection key of logit v of expert e: the high word orders the float (-0 ranks equal
+// to +0), the low word holds 0xFFFFFFFF - e so equal logits resolve to the lower expert index.
+// Keys of one token's experts are distinct; its top-k are the k largest keys.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -93,6 +100,76 @@ __device__ __forceinline__ QScale block_scale(float amax) {
         q.inv = 1.0f / q.scale;
     }
     return q;
+}
+
+// Quantise 8 consecutive bf16 values (one 16-byte load) that belong to a 128-value block
+// spread over an aligned group of 16 lanes: the block amax is reduced over the group, then
+// every value is encoded with the block's reciprocal scale.  Lanes with valid == false add
+// nothing to the amax.
+struct Quant8 {
+    uint2 codes;
+    float scale;
+};
+
+__device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = max16(valid ? amax : 0.0f);
+    const QScale q = block_scale(amax);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(v[i] * q.inv);
+    Quant8 out;
+    out.codes.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    out.codes.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    out.scale = q.scale;
+    return out;
+}
+
+// ---- matrix-core operands and vector-memory ordering ----
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i pack8(uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ v8i pack8v(u32x4 lo, u32x4 hi) {
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima): gfx9 encoding,
+// vmcnt bits [3:0] and [15:14]
+#define MOE_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Workgroup barrier that leaves the newest VM vector-memory operations of each wave in flight.
+// Every LDS operation has completed (lgkmcnt 0) and every LDS DMA older than those VM loads
+// has landed (DMA counts in vmcnt and decrements once its data is in LDS), so what was written
+// to LDS before it is visible after it.  The compiler's own barrier would drain vmcnt to zero
+// and with it a weight stream in flight; the signal fences only keep the compiler from moving
+// memory operations across the barrier.
+template <int VM>
+__device__ __forceinline__ void barrier_keep_vm() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 }  // namespace moe

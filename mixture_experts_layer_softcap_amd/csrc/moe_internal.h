@@ -48,6 +48,17 @@ hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int ro
                                  int epilogue, const int32_t* sorted, void* out,
                                  hipStream_t s);
 
+// small-batch forward GEMM with the layout, sort/gather and quantisation folded in: weight
+// slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])
+bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows);
+hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
+                                 const uint8_t* w, const float* w_scales, int N,
+                                 float* rows_out, hipStream_t s);
+
+// per-expert counts [E] and exclusive offsets [E+1] of the routed ids (E <= 1024)
+hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* counts,
+                         int32_t* offsets, hipStream_t s);
+
 // BF16 grouped GEMM (256 x 256 tiles; STORE_F32, STORE_BF16, SWIGLU_BF16)
 hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,

@@ -17,34 +17,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSpan = kThreads * 8;  // elements of one row covered per pass
 
-struct Quant8 {
-    uint2 codes;
-    float scale;
-};
-
-__device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
-    float v[8];
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = max16(valid ? amax : 0.0f);
-    const QScale q = block_scale(amax);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(v[i] * q.inv);
-    Quant8 out;
-    out.codes.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    out.codes.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    out.scale = q.scale;
-    return out;
-}
-
 __global__ __launch_bounds__(kThreads) void qsg_kernel(
     const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ ids, int k, int E,
     int32_t* __restrict__ cursors, int32_t* __restrict__ sorted_route_ids,

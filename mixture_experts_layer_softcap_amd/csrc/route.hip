@@ -13,13 +13,6 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u) u = 0u;                          // -0 ranks equal to +0
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int M,
                                                     int E, int k, float softcap,

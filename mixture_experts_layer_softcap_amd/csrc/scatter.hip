@@ -15,6 +15,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The k routes of a token are read in groups of kGroup: every load of a group (ids, weights,
+// slots, rows) is issued before any is used, so a group costs one round trip (two with a slot
+// table), whatever the ids hold; indices past k or behind an invalid id are clamped and their
+// terms skipped.
+constexpr int kGroup = 8;
+
+template <bool SLOTS>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const float* __restrict__ rows, const int32_t* __restrict__ route_slots,
     const float* __restrict__ weights, const int32_t* __restrict__ ids, int M, int k, int E,
@@ -25,16 +32,34 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const int t = (int)(idx / quads);
     const int n = (int)(idx % quads) * 4;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int j = 0; j < k; ++j) {
-        const size_t r = (size_t)t * k + j;
-        if ((unsigned)ids[r] >= (unsigned)E) continue;
-        const size_t row = route_slots ? (size_t)route_slots[r] : r;
-        const float w = weights[r];
-        const float4 v = *reinterpret_cast<const float4*>(rows + row * N + n);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        int e[kGroup];
+        float wv[kGroup];
+        size_t row[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const size_t r = (size_t)t * k + min(j0 + u, k - 1);
+            e[u] = ids[r];
+            wv[u] = weights[r];
+            row[u] = r;
+            if (SLOTS) {
+                const int sl = route_slots[r];          // -1 behind an invalid id
+                row[u] = sl < 0 ? 0 : (size_t)sl;
+            }
+        }
+        float4 v[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+            v[u] = *reinterpret_cast<const float4*>(rows + row[u] * N + n);
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            if (j0 + u < k && (unsigned)e[u] < (unsigned)E) {
+                acc.x += wv[u] * v[u].x;
+                acc.y += wv[u] * v[u].y;
+                acc.z += wv[u] * v[u].z;
+                acc.w += wv[u] * v[u].w;
+            }
+        }
     }
     uint2 o;
     o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
@@ -50,8 +75,12 @@ hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const f
     const size_t work = (size_t)M * (N / 4);
     if (work == 0) return hipSuccess;
     const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(scatter_kernel, dim3(grid), dim3(kThreads), 0, s, rows, route_slots,
-                       weights, ids, M, k, E, N, out);
+    if (route_slots)
+        hipLaunchKernelGGL(scatter_kernel<true>, dim3(grid), dim3(kThreads), 0, s, rows,
+                           route_slots, weights, ids, M, k, E, N, out);
+    else
+        hipLaunchKernelGGL(scatter_kernel<false>, dim3(grid), dim3(kThreads), 0, s, rows,
+                           route_slots, weights, ids, M, k, E, N, out);
     return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ MOE_EPI_SWIGLU_BF16 = 3
 
 MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
+MOE_FWD_STAGED = 4
 
 # entry points and their C signatures (names identical to include/moe.h)
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -44,6 +45,8 @@ SIGNATURES = {
     "moe_gemm_n_tile": (_I, [_I]),
     "moe_grouped_gemm": (_I, [_I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I,
                               _P, _P, _P]),
+    "moe_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I, _I]),
+    "moe_grouped_gemm_routed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
     "moe_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
@@ -152,6 +155,25 @@ def grouped_gemm(mode: int, a, a_scales, w, w_scales, tasks, ntasks, chunk_rows:
     _call("moe_grouped_gemm", mode, _ptr(a), _ptr(a_scales), rows, K, _ptr(w), _ptr(w_scales),
           E, N, _ptr(tasks), _ptr(ntasks), tasks.shape[0], chunk_rows, _ptr(queue), epilogue,
           _ptr(sorted_route_ids), _ptr(out), _stream(stream))
+
+
+def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
+                    flags: int = 0) -> int:
+    """Kernels moe_forward_ex launches for these arguments (3 small-batch path, 5 staged)."""
+    n = lib().moe_forward_kernels(M, E, k, K, N, chunk_rows, flags)
+    if n < 0:
+        raise MoeError("moe_forward_kernels", n)
+    return n
+
+
+def grouped_gemm_routed(x, topk_ids, E: int, w_q, w_scales, rows, counts=None, offsets=None,
+                        stream=None):
+    """Small-batch grouped FP8 GEMM straight from routed ids (moe_grouped_gemm_routed)."""
+    M, K = x.shape
+    k = topk_ids.shape[1]
+    N = w_q.shape[1]
+    _call("moe_grouped_gemm_routed", _ptr(x), _ptr(topk_ids), M, k, E, K, _ptr(w_q),
+          _ptr(w_scales), N, _ptr(rows), _ptr(counts), _ptr(offsets), _stream(stream))
 
 
 def scatter(rows, topk_weights, topk_ids, E: int, out, route_slots=None, stream=None):

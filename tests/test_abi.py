@@ -99,7 +99,7 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     ws = L.moe_forward_workspace_bytes(8, 16, 2, 256, 256)
     f = L.moe_forward_ex
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC
-    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 4, S) == INVAL     # flags
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 8, S) == INVAL     # flags
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 65, 0, S) == INVAL    # chunk
     assert f(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 0, S) == INVAL
     assert L.moe_forward(P, P, P, P, 0, 16, 2, 256, 256, 30.0, P, P, ws, S) == INVAL

@@ -22,6 +22,7 @@ TINY = "fused_fp8_M8_E16_k2_K256_N256"
 QWEN = "fused_fp8_M128_E256_k8_K2048_N512"
 ZIPF1K = "fused_fp8_M1024_E256_k8_K2048_N512_zipf"
 ZIPF4K = "fused_fp8_M4096_E256_k8_K2048_N512_zipf"
+TINY_K2048 = "M24_E40_k3_K2048_N256"
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -322,6 +323,77 @@ def test_gemm_qwen_layer_rows():
         assert_gemm_f32_close(got, C, f"chunk={chunk} queue={queue}")
 
 
+def routed_case(name):
+    """Inputs of the fused small-batch GEMM: a named workload, or (M, E, k, N, bias) at K=2048."""
+    if isinstance(name, str):
+        return workload(name)
+    M, E, k, N, bias = name
+    d = synth.fused_inputs(M, E, k, 2048, N, seed=M + E, bias=bias)
+    d.update(M=M, E=E, k=k, K=2048, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    return d
+
+
+@pytest.mark.parametrize("name", [
+    QWEN,
+    (24, 40, 3, 256, None),     # 1.8 rows per expert; workgroup ranges cross expert boundaries
+    (256, 16, 8, 256, None),    # 128 rows per expert: 8 tiles, two rounds of resident tiles
+    (200, 64, 6, 384, "zipf"),  # skewed: a hot expert with several tiles, many with one
+    (300, 600, 2, 128, None),   # more experts than CUs: ranges of several experts
+    (1024, 64, 2, 256, None),   # 2048 routed rows, the most the kernel takes
+])
+def test_gemm_routed_matches_staged_oracle(name):
+    # the fused small-batch GEMM: layout, sort/gather and quantisation inside the kernel; its
+    # rows sit at route ids, so the oracle's sorted rows are permuted back before comparing
+    d = routed_case(name)
+    M, E, k, K, N = d["M"], d["E"], d["k"], d["K"], d["N"]
+    ids, _ = orc.route(d["logits"], k, CAP)
+    counts, offsets = orc.layout(ids, E)
+    q, s = orc.quant_act(d["x"])
+    sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
+    C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
+    ref = np.zeros_like(C)
+    ref[sorted_ids] = C
+    rows = zeros((M * k, N), torch.float32)
+    cnt, off = zeros((E,), torch.int32), zeros((E + 1,), torch.int32)
+    moe.grouped_gemm_routed(to_dev(d["x"]), to_dev(ids), E, to_dev(d["w_q"]), to_dev(d["w_s"]),
+                            rows, cnt, off)
+    sync()
+    np.testing.assert_array_equal(to_np(cnt), counts)
+    np.testing.assert_array_equal(to_np(off), offsets)
+    assert_gemm_f32_close(to_np(rows), ref, f"routed {name}")
+
+
+def test_gemm_routed_invalid_ids_and_repeat():
+    # ids outside [0, E) route nowhere: their rows stay untouched; a second call on the same
+    # buffers gives the same bits (no state kept between calls); counts/offsets may be NULL
+    M, E, k, N = 40, 24, 4, 256
+    d = routed_case((M, E, k, N, None))
+    ids, _ = orc.route(d["logits"], k, CAP)
+    bad = ids.copy()
+    bad[3, 1], bad[17, 0], bad[39, 3] = -1, E, 1 << 20
+    valid = (bad >= 0) & (bad < E)
+    # a route's row depends only on its token and expert: the reference of the clean ids
+    # holds every row the kernel must write
+    counts, offsets = orc.layout(ids, E)
+    q, s = orc.quant_act(d["x"])
+    sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
+    C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
+    ref = np.zeros_like(C)
+    ref[sorted_ids] = C
+    flat = valid.reshape(-1)
+    outs = []
+    for _ in range(2):
+        rows = torch.full((M * k, N), 7.0, dtype=torch.float32, device="cuda")
+        moe.grouped_gemm_routed(to_dev(d["x"]), to_dev(bad), E, to_dev(d["w_q"]),
+                                to_dev(d["w_s"]), rows)
+        sync()
+        outs.append(to_np(rows))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    assert (outs[0][~flat] == 7.0).all()
+    assert_gemm_f32_close(outs[0][flat], ref[flat], "routed, invalid ids")
+
+
 # ---- stage 5: scatter --------------------------------------------------------------------
 
 def test_scatter_matches_oracle():
@@ -363,7 +435,8 @@ def ws_part(ws, d, which, dtype, count):
     return to_np(ws[off:off + nbytes]).view(dtype)
 
 
-@pytest.mark.parametrize("flags", [0, moe.MOE_FWD_GRAPH, moe.MOE_FWD_STATIC_GRID])
+@pytest.mark.parametrize("flags", [0, moe.MOE_FWD_GRAPH, moe.MOE_FWD_STATIC_GRID,
+                                   moe.MOE_FWD_STAGED])
 @pytest.mark.parametrize("name", [TINY, QWEN])
 def test_forward_full(name, flags):
     d = workload(name)
@@ -376,8 +449,12 @@ def test_forward_full(name, flags):
     R = d["M"] * d["k"]
     np.testing.assert_array_equal(ws_part(ws, d, 0, np.int32, R).reshape(d["M"], d["k"]),
                                   ref["ids"])
-    np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, d["E"]), ref["counts"])
-    np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, d["E"] + 1), ref["offsets"])
+    M, E, k, K, N = d["M"], d["E"], d["k"], d["K"], d["N"]
+    if moe.forward_kernels(M, E, k, K, N, 0, flags) == 5:  # the small-batch path has no layout
+        np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, d["E"]), ref["counts"])
+        np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, d["E"] + 1), ref["offsets"])
+    else:
+        assert not flags & moe.MOE_FWD_STAGED and name == QWEN
 
 
 @pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
@@ -405,6 +482,9 @@ def test_forward_skewed_sampled(name):
     (64, 8, 1, 384, 256, "one"),       # every route on one expert -> several chunks
     (200, 300, 3, 128, 384, None),     # E not a multiple of 64, empty experts
     (17, 64, 4, 2176, 128, None),      # K over one 2048 pass, ragged
+    (100, 300, 3, 2048, 384, None),    # fused small-batch path: E not a multiple of 64, Nb=3
+    (512, 512, 4, 2048, 128, None),    # fused path at its limits (2048 routes, 512 experts,
+                                       # one panel): ranges span several tile rounds
 ])
 def test_forward_edge_shapes(M, E, k, K, N, bias):
     b = None
@@ -415,7 +495,7 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
     d.update(M=M, E=E, k=k, K=K, N=N)
     d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
     ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
-    for flags in (0, moe.MOE_FWD_STATIC_GRID):
+    for flags in (0, moe.MOE_FWD_STATIC_GRID, moe.MOE_FWD_STAGED):
         y = gpu_forward(d, flags=flags)[0]
         assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N}")
 
