@@ -131,7 +131,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     // ids goes a small first burst: the first kPre units of the wave's first slice of the
     // range (unless routing moves the wave's start, the slice it will stream first).  It keeps
     // the memory busy while the tiles are built, yet drains before the x rows are requested.
-    constexpr int kPre = 2;
+    constexpr int kPre = 4;
     const int s_pre = min(lo + wave, hi - 1);
     int v[4];
 #pragma unroll

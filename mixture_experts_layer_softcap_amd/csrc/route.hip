@@ -3,52 +3,87 @@
 // topk_weights feed the combine).
 //
 // One wave64 per token, E/64 logits per lane held in registers.  Selection runs on the raw
-// fp32 logit (softcap and softmax are strictly increasing, so the top-k is the same) as k
-// rounds of a wave-wide argmax over a 64-bit key: the high word orders the float, the low
-// word holds 0xFFFFFFFF - e so equal logits resolve to the lower expert index.  tanh and exp
-// run only for the k winners, on lanes 0..k-1.
+// fp32 logit (softcap and softmax are strictly increasing, so the top-k is the same), ordered
+// by its monotone 32-bit image and, between equal logits, by the lower expert index: k rounds
+// of a wave-wide maximum of the image (DPP row shifts and row broadcasts, no LDS), then one
+// ballot per register for the lowest-index holder of that maximum, which is retired.  tanh
+// and exp run only for the k winners, on lanes 0..k-1.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
+constexpr int kRouteWaves = 4;
+
+// monotone 32-bit image of a logit (the high word of route_key)
+__device__ __forceinline__ uint32_t logit_ord(float v) { return (uint32_t)(route_key(v, 0) >> 32); }
+
+// maximum over the 64 lanes: inclusive max-scans inside each row of 16 lanes (row_shr 1, 2, 4,
+// 8), then the row totals carried across rows (row_bcast 15 into rows 1 and 3, row_bcast 31
+// into rows 2 and 3); lane 63 ends with the wave's maximum.  Lanes a shift leaves without a
+// source take 0, which is below or equal to every image.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_DPP_MAX(ctrl, rows) \
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rows, 0xf, false))
+    MOE_DPP_MAX(0x111, 0xf);
+    MOE_DPP_MAX(0x112, 0xf);
+    MOE_DPP_MAX(0x114, 0xf);
+    MOE_DPP_MAX(0x118, 0xf);
+    MOE_DPP_MAX(0x142, 0xa);
+    MOE_DPP_MAX(0x143, 0xc);
+#undef MOE_DPP_MAX
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 template <int VPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int M,
-                                                    int E, int k, float softcap,
-                                                    int32_t* __restrict__ ids,
-                                                    float* __restrict__ weights) {
+__global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
+    const float* __restrict__ logits, int M, int E, int k, float softcap,
+    int32_t* __restrict__ ids, float* __restrict__ weights) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
     if (t >= M) return;
     const float* row = logits + (size_t)t * E;
 
-    uint64_t key[VPL];
+    float val[VPL];
+    uint32_t ord[VPL];
+    uint64_t avail[VPL];                        // experts not yet taken (bit per lane)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) val[i] = row[min(lane + 64 * i, E - 1)];   // clamped
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = (e < E) ? route_key(row[e], e) : 0ull;   // 0 sorts below every valid key
+        ord[i] = logit_ord(val[i]);
+        avail[i] = __ballot(lane + 64 * i < E);
     }
 
     int my_e = 0;
     float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint64_t o = __shfl_xor(best, off);
-            best = o > best ? o : best;
-        }
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-        // retire the winner in the lane that holds it
+        uint32_t loc = 0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
-            if (lane + 64 * i == e) key[i] = 0ull;
+            loc = max(loc, (avail[i] >> lane) & 1ull ? ord[i] : 0u);
+        const uint32_t m = wave_max_u32(loc);
+        // the lowest-index available expert holding the maximum
+        int win_i = -1, win_l = 0;
+#pragma unroll
+        for (int i = VPL - 1; i >= 0; --i) {
+            const uint64_t hit = __ballot(ord[i] == m) & avail[i];
+            if (hit) {
+                win_i = i;
+                win_l = __builtin_ctzll(hit);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (i == win_i) avail[i] &= ~(1ull << win_l);
+        float wl = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (i == win_i) wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), win_l));
         if (lane == j) {
-            my_e = e;
-            my_l = row[e];
+            my_e = win_l + 64 * win_i;
+            my_l = wl;
         }
     }
 
@@ -67,9 +102,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                       float* weights, hipStream_t s) {
-    const int grid = (M + 3) / 4;
-    hipLaunchKernelGGL(route_kernel<VPL>, dim3(grid), dim3(256), 0, s, logits, M, E, k,
-                       softcap, ids, weights);
+    const int grid = (M + kRouteWaves - 1) / kRouteWaves;
+    hipLaunchKernelGGL(route_kernel<VPL>, dim3(grid), dim3(64 * kRouteWaves), 0, s, logits, M,
+                       E, k, softcap, ids, weights);
     return hipGetLastError();
 }
 
