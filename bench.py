@@ -331,7 +331,7 @@ def main():
         return ws[o:o + n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
     R = M * k
-    chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (32 if -(-R // E) <= 48 else 64))
+    chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if K <= 8192 else 64))
     fused = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags) == 3
     rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
     if fused:
@@ -364,6 +364,8 @@ def main():
         gemm_kernel = "gemm_fp8_fused_kernel (grouped FP8 GEMM from routed ids, rows at route ids)"
     elif K == 2048 and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
+    elif 64 < chunk <= 256 and K <= 8192:
+        gemm_kernel = "gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles, ROUTE_F32)"
     else:
         gemm_kernel = "gemm_fp8_kernel (grouped FP8 GEMM, ROUTE_F32)"
     lbytes = layer_algorithmic_bytes(counts, M, E, k, K, N)
@@ -388,6 +390,8 @@ def main():
                    "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
                                       else "contiguous ranges, per-wave pull"
                                       if K == 2048 and chunk <= 16
+                                      else "one task per workgroup, chunks spread over XCDs"
+                                      if 64 < chunk <= 256 and K <= 8192
                                       else "static stride" if args.static_grid else "atomic queue"),
                    "launch": "graph" if args.graph else "plain",
                    "chunk_rows": chunk},

@@ -154,11 +154,14 @@ int moe_gemm_n_tile(int mode);
  * *ntasks exit at once); queue is not used.
  * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 2048 the task list is cut into one
  * contiguous range of 16-column subtasks per workgroup, balanced inside the workgroup by an
- * LDS counter; queue is not used.  Otherwise, with queue != NULL, a persistent grid pulls
+ * LDS counter; queue is not used.  For chunk_rows in [65, 256] (K <= 8192) one workgroup
+ * runs one task with both operands staged in LDS (grid = max_tasks rounded up to whole
+ * chunks per XCD; workgroups past *ntasks exit at once; the panels of one chunk run on one
+ * XCD); queue is not used.  Otherwise, with queue != NULL, a persistent grid pulls
  * task indices from queue[0] with atomics and the last workgroup to leave resets
  * queue[0..1] to zero, so the call can be repeated or graph-replayed; with queue == NULL
  * the same grid walks the task list with a fixed stride.  Tasks must come from
- * moe_build_layout for the same rows, E, n_tile and chunk_rows (FP8_B128: chunk_rows <= 64):
+ * moe_build_layout for the same rows, E, n_tile and chunk_rows (FP8_B128: chunk_rows <= 256):
  * all n_blocks panels of one chunk consecutive.  Each task streams its expert's weight panel
  * once. */
 int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
@@ -211,7 +214,8 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
                 const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                 uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
-/* moe_forward with explicit options: chunk_rows (0 = chosen from M*k/E), flags bit 0 = replay
+/* moe_forward with explicit options: chunk_rows (0 = 16 while M*k/E <= 16, else 128 for
+ * K <= 8192 or 64), flags bit 0 = replay
  * a HIP graph captured once per (shape, softcap, pointers, options) instead of launching the
  * kernels (ignored while the caller's stream is being captured), bit 1 = fixed-stride task
  * walk instead of the atomic queue (grouped GEMM forms that walk a queue). */

@@ -108,11 +108,12 @@ bool forward_dims_ok(int M, int E, int k, int K, int N) {
            N % 128 == 0 && (long long)M * k * (long long)K < (1LL << 40);
 }
 
-int default_chunk(int M, int k, int E) {
+// Task chunk of the forward's grouped GEMM: 16 routed rows (the streaming forms) while experts
+// average at most 16 rows, else 128 (the LDS-tiled form; K <= 8192) or 64 (the general form).
+int default_chunk(int M, int k, int E, int K) {
     const long long avg = ((long long)M * k + E - 1) / E;
     if (avg <= 16) return 16;
-    if (avg <= 48) return 32;
-    return 64;
+    return K <= 8192 ? 128 : 64;
 }
 
 // ---- the enqueued step -----------------------------------------------------------------
@@ -381,7 +382,7 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
     if (mode != MOE_GEMM_FP8_B128) return MOE_E_INVAL;
     if (rows < 0 || E < 1 || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
         return MOE_E_INVAL;
-    if (chunk_rows < 1 || chunk_rows > 64) return MOE_E_INVAL;
+    if (chunk_rows < 1 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
     if (epilogue != MOE_EPI_STORE_F32 && epilogue != MOE_EPI_STORE_BF16 &&
         epilogue != MOE_EPI_ROUTE_F32)
         return MOE_E_INVAL;
@@ -440,13 +441,13 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
     if (!logits || !x || !w_q || !w_scales || !out || !workspace) return MOE_E_INVAL;
     if (softcap != softcap) return MOE_E_INVAL;
-    if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
+    if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
     if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
     if (workspace_bytes < ws_layout(M, E, k, K, N).total) return MOE_E_NOSPC;
     int rc = check_device();
     if (rc) return rc;
     FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
-              chunk_rows ? chunk_rows : default_chunk(M, k, E), flags};
+              chunk_rows ? chunk_rows : default_chunk(M, k, E, K), flags};
     hipStream_t s = (hipStream_t)stream;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
@@ -460,11 +461,11 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
 
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags) {
     if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
-    if (chunk_rows < 0 || chunk_rows > 64) return MOE_E_INVAL;
+    if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
     if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
-    const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E);
+    const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
     return !(flags & MOE_FWD_STAGED) && forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
 

@@ -90,18 +90,19 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     const int nk = K / kBK;
 
     // Operand tiles in LDS, per stage: [256 rows][128 bytes] for A and for W (the stage's 64
-    // k values of each row), the 16-byte chunk c of row r stored at position c ^ (r % 8).  A DMA
-    // instruction moves 8 whole 128-byte row segments (lane l: row l/8, position l%8, so
-    // global chunk (l%8) ^ (l/8)); every line it touches is read in full.  An MFMA fragment
-    // read (lane (j, h): row g*32 + j, chunk 2s + h) hits 8 distinct positions in every 8
-    // consecutive rows, so it is free of bank conflicts.
+    // k values of each row), the 16-byte chunk c of row r stored at position c ^ ((r/2) % 8).
+    // A DMA instruction moves 8 whole 128-byte row segments (lane l: row l/8, position l%8);
+    // every line it touches is read in full.  The LDS serves a 16-byte read for 16 lanes per
+    // clock over 64 four-byte banks, i.e. two 128-byte rows side by side: an MFMA fragment read
+    // (lanes j..j+15 of one half h: rows g*32 + j, one chunk 2s + h) then has rows of equal
+    // parity at 8 distinct positions, so it is free of bank conflicts.
     const int dl = lane >> 3;                   // row within a DMA instruction
-    const int dc = (lane & 7) ^ dl;             // global 16-byte chunk this lane moves
     const uint16_t* srcA[8];
     const uint16_t* srcW[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = wave * 64 + i * 8 + dl;   // tile row moved by this lane
+        const int dc = (lane & 7) ^ ((r >> 1) & 7);   // global 16-byte chunk this lane moves
         srcA[i] = a + (size_t)(rb + min(r, rc - 1)) * K + dc * 8;
         int wr;
         if (EPI == MOE_EPI_SWIGLU_BF16)
@@ -141,7 +142,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     uint32_t pa[4], pw0[4], pw2[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        const uint32_t in_row = (uint32_t)(j * 128 + (((2 * st + h) ^ (j & 7)) << 4));
+        const uint32_t in_row = (uint32_t)(j * 128 + (((2 * st + h) ^ ((j >> 1) & 7)) << 4));
         pa[st] = baseA + (uint32_t)(4 * wm) * 4096u + in_row;
         pw0[st] = baseW + (uint32_t)wg0 * 4096u + in_row;
         pw2[st] = baseW + (uint32_t)wg2 * 4096u + in_row;

@@ -322,6 +322,9 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, in
     if (gemm_fp8_range_applies(K, chunk_rows))
         return launch_gemm_fp8_range(a, a_scales, rows, K, w, w_scales, N, tasks, ntasks,
                                      max_tasks, epilogue, sorted_route_ids, out, s);
+    if (gemm_fp8_tile_applies(K, chunk_rows))
+        return launch_gemm_fp8_tile(a, a_scales, rows, K, w, w_scales, N, tasks, ntasks,
+                                    max_tasks, chunk_rows, epilogue, sorted_route_ids, out, s);
     LaunchArgs A{a, a_scales, w, w_scales, tasks, ntasks, queue, sorted_route_ids, out,
                  rows, K, N, epilogue};
     int grid = device_info().cu_count;      // one 8-wave workgroup per CU

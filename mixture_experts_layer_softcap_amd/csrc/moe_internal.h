@@ -48,6 +48,14 @@ hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int ro
                                  int epilogue, const int32_t* sorted, void* out,
                                  hipStream_t s);
 
+// tiled form for chunks of 65..256 routed rows (both operands staged in LDS)
+bool gemm_fp8_tile_applies(int K, int chunk_rows);
+hipError_t launch_gemm_fp8_tile(const uint8_t* a, const float* a_scales, int rows, int K,
+                                const uint8_t* w, const float* w_scales, int N,
+                                const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                                int chunk_rows, int epilogue, const int32_t* sorted, void* out,
+                                hipStream_t s);
+
 // small-batch forward GEMM with the layout, sort/gather and quantisation folded in: weight
 // slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])
 bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows);

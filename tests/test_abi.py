@@ -91,7 +91,8 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert L.moe_quantize_weights(NULL, 2, 128, 256, P, P, S) == INVAL
     gg = L.moe_grouped_gemm
     assert gg(7, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # mode
-    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 65, P, 0, P, P, S) == INVAL  # chunk
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 257, P, 0, P, P, S) == INVAL  # chunk
+    assert gg(0, P, P, 4, 8320, P, P, 2, 256, P, P, 8, 65, P, 0, P, P, S) == INVAL  # tiled K
     assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 9, P, P, S) == INVAL  # epilogue
     assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 2, NULL, P, S) == INVAL  # route ids
     assert gg(0, P, P, 4, 250, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # K % 128
@@ -100,7 +101,7 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     f = L.moe_forward_ex
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 8, S) == INVAL     # flags
-    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 65, 0, S) == INVAL    # chunk
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 257, 0, S) == INVAL   # chunk
     assert f(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 0, S) == INVAL
     assert L.moe_forward(P, P, P, P, 0, 16, 2, 256, 256, 30.0, P, P, ws, S) == INVAL
     assert L.moe_sort_gather_bf16(P, 4, 100, P, 2, 8, P, P, P, P, S) == INVAL   # K % 8

@@ -273,9 +273,12 @@ def gpu_gemm(a_q, a_s, w_q, w_s, offsets, chunk, epilogue, sorted_ids=None, queu
 @pytest.mark.parametrize("chunk,queue,K", [(16, True, 512), (16, False, 512), (32, True, 512),
                                            (64, True, 512), (5, True, 512), (16, True, 2048),
                                            (16, False, 2048), (7, False, 4096),
-                                           (3, True, 4096), (64, False, 2048)])
+                                           (3, True, 4096), (64, False, 2048),
+                                           (128, True, 512), (256, False, 2048),
+                                           (200, True, 4096), (256, True, 128)])
 def test_gemm_integer_exact(chunk, queue, K):
-    # K in {2048, 4096} with chunk <= 16 takes the streaming kernel, the rest the general one
+    # K in {2048, 4096} with chunk <= 16 takes the streaming kernel, chunks of 65..256 rows the
+    # LDS-tiled kernel, the rest the general one
     g = np.random.default_rng(chunk + K)
     E, N = 4, 256
     counts = np.array([3, 0, 37, 70], np.int32)
@@ -291,6 +294,30 @@ def test_gemm_integer_exact(chunk, queue, K):
     got = gpu_gemm(int_codes(Ai), sa, int_codes(Wi), sb, offsets, chunk,
                    moe.MOE_EPI_STORE_F32, queue=queue, repeat=2)
     np.testing.assert_array_equal(got, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("chunk", [80, 256])
+def test_gemm_tiled_multi_chunk_epilogues(chunk):
+    # experts of 0, 1, 255, 256, 257 and 600 rows: full 256-row tiles, a one-row tile, ragged
+    # tails inside 16- and 8-row groups; integer data with power-of-two scales is exact
+    g = np.random.default_rng(chunk)
+    E, N, K = 6, 384, 640
+    counts = np.array([0, 1, 255, 256, 257, 600], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    Ai = g.integers(-4, 5, (rows, K))
+    Wi = g.integers(-4, 5, (E, N, K))
+    sa = np.exp2(g.integers(-1, 2, (K // 128, rows))).astype(np.float32)
+    sb = np.exp2(g.integers(-1, 2, (E, N // 128, K // 128))).astype(np.float32)
+    ref = orc.gemm_fp8(int_codes(Ai), sa, int_codes(Wi), sb, offsets).astype(np.float32)
+    a_q, w_q = int_codes(Ai), int_codes(Wi)
+    got = gpu_gemm(a_q, sa, w_q, sb, offsets, chunk, moe.MOE_EPI_STORE_F32, repeat=2)
+    np.testing.assert_array_equal(got, ref)
+    b16 = gpu_gemm(a_q, sa, w_q, sb, offsets, chunk, moe.MOE_EPI_STORE_BF16).view(np.uint16)
+    np.testing.assert_array_equal(b16, synth.bf16_bits(ref))
+    perm = g.permutation(rows).astype(np.int32)     # a route id per sorted row
+    rt = gpu_gemm(a_q, sa, w_q, sb, offsets, chunk, moe.MOE_EPI_ROUTE_F32, sorted_ids=perm)
+    np.testing.assert_array_equal(rt[perm], ref)
 
 
 def test_gemm_random_store_modes():
@@ -317,7 +344,7 @@ def test_gemm_qwen_layer_rows():
     q, s = orc.quant_act(d["x"])
     sorted_ids, a_q, a_s = orc.sort_gather(ids, offsets, q, s)
     C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], offsets)
-    for chunk, queue in ((16, True), (16, False), (64, True)):
+    for chunk, queue in ((16, True), (16, False), (64, True), (256, True)):
         got = gpu_gemm(a_q, a_s, d["w_q"], d["w_s"], offsets, chunk, moe.MOE_EPI_STORE_F32,
                        queue=queue)
         assert_gemm_f32_close(got, C, f"chunk={chunk} queue={queue}")
@@ -457,13 +484,14 @@ def test_forward_full(name, flags):
         assert not flags & moe.MOE_FWD_STAGED and name == QWEN
 
 
+@pytest.mark.parametrize("chunk", [0, 64, 256])
 @pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
-def test_forward_skewed_sampled(name):
+def test_forward_skewed_sampled(name, chunk):
     d = workload(name)
     ids, _ = orc.route(d["logits"], d["k"], CAP)
     counts, _ = orc.layout(ids, d["E"])
     assert counts.min() >= 1 and counts.max() / counts.min() >= 10
-    outs = gpu_forward(d, reps=2)
+    outs = gpu_forward(d, reps=2, chunk=chunk)
     # sampled tokens: first, last, a seeded spread, and tokens routed to the busiest expert
     busiest = int(np.argmax(counts))
     on_busy = np.nonzero((ids == busiest).any(1))[0]
@@ -495,9 +523,10 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
     d.update(M=M, E=E, k=k, K=K, N=N)
     d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
     ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
-    for flags in (0, moe.MOE_FWD_STATIC_GRID, moe.MOE_FWD_STAGED):
-        y = gpu_forward(d, flags=flags)[0]
-        assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N}")
+    for flags, chunk in ((0, 0), (moe.MOE_FWD_STATIC_GRID, 0), (moe.MOE_FWD_STAGED, 0),
+                        (0, 256), (0, 100)):
+        y = gpu_forward(d, flags=flags, chunk=chunk)[0]
+        assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N} chunk={chunk}")
 
 
 def test_forward_repeat_determinism():
