@@ -68,16 +68,22 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def gemm_algorithmic_bytes(counts, M, k, K, N, fused=False):
+def gemm_algorithmic_bytes(counts, M, k, K, N, fused=False, gather=False):
     """Bytes the grouped GEMM must move: each non-empty expert's FP8 weights and scales once,
     the fp32 routed output rows once, and its inputs once: the routed FP8 rows, their scales
-    and sorted ids (staged), or the bf16 token rows and the routed ids (fused: layout, gather
-    and quantisation inside the GEMM)."""
+    and sorted ids (staged), the token-major FP8 rows, their scales and the sorted ids
+    (gather), or the bf16 token rows and the routed ids (fused: layout, gather and
+    quantisation inside the GEMM)."""
     nonempty = int((counts > 0).sum())
     R = M * k
     Nb, Kb = N // 128, K // 128
     weights = nonempty * (N * K + Nb * Kb * 4)
-    acts = M * K * 2 + R * 4 if fused else R * K + Kb * R * 4 + R * 4
+    if fused:
+        acts = M * K * 2 + R * 4
+    elif gather:
+        acts = M * K + Kb * M * 4 + R * 4
+    else:
+        acts = R * K + Kb * R * 4 + R * 4
     out = R * N * 4
     return weights + acts + out
 
@@ -332,9 +338,23 @@ def main():
 
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if K <= 8192 else 64))
-    fused = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags) == 3
+    nkern = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags)
+    fused, gather = nkern == 3, nkern == 4
     rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
-    if fused:
+    if gather:
+        # the step's tiled GEMM on what the last step left in the workspace: token-major codes
+        # and scales, the task list and the sorted route ids
+        x_q = wsp(13, torch.uint8, M * K).view(M, K)
+        x_s = wsp(14, torch.float32, (K // 128) * M)
+        max_tasks = moe.max_tasks(M, k, E, N // 128, chunk)
+        tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
+        ntasks = wsp(6, torch.int32, 1)
+        sorted_ids = wsp(8, torch.int32, R)
+
+        def gemm(i):
+            moe.grouped_gemm_gather(x_q, x_s, k, wqs[i % copies], wss[i % copies], tasks, ntasks,
+                                    chunk, sorted_ids, rows_out)
+    elif fused:
         # the step's GEMM reads the routed ids (workspace part 0, written by its route stage)
         ids_ws = wsp(0, torch.int32, R).view(M, k)
 
@@ -357,10 +377,13 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     gemm_us = g0.elapsed_time(g1) * 1e3 / args.steps
-    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N, fused)
+    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N, fused, gather)
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
 
-    if fused:
+    if gather:
+        gemm_kernel = ("gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles gathered from "
+                       "token-major rows, ROUTE_F32)")
+    elif fused:
         gemm_kernel = "gemm_fp8_fused_kernel (grouped FP8 GEMM from routed ids, rows at route ids)"
     elif K == 2048 and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
@@ -386,6 +409,8 @@ def main():
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
                    "path": ("3 kernels: route, grouped GEMM from the routed ids, combine" if fused
+                            else "4 kernels: route+quantise, layout+sort, gathering grouped "
+                                 "GEMM, combine" if gather
                             else "5 kernels: route, layout, QSG, grouped GEMM, combine"),
                    "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
                                       else "contiguous ranges, per-wave pull"

@@ -81,6 +81,15 @@ int moe_device_check(void);
 int moe_route(const float* logits, int M, int E, int k, float softcap, int32_t* topk_ids,
               float* topk_weights, moe_stream_t stream);
 
+/* moe_route plus the blockwise E4M3 quantisation of every token's row of x, once per token
+ * ([FMF8] Baseline item 4 with the moe_quant_sort_gather rule below, without the sort and
+ * the k copies): x bf16 [M][K] -> x_q E4M3 [M][K] and x_scales f32 [K/128][M] (scale of
+ * token t, block b at x_scales[b*M + t]).  K a multiple of 128.  moe_grouped_gemm_gather
+ * reads the routed rows from these by token.  One launch. */
+int moe_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k, int K,
+                       float softcap, int32_t* topk_ids, float* topk_weights, uint8_t* x_q,
+                       float* x_scales, moe_stream_t stream);
+
 /* ---- [FMF8] Baseline items 2-3 + Fusion 3 (count and build layout), [WEAVE] 4.3 ---------
  * Host only (no HIP call): capacity that `tasks` needs for moe_build_layout, i.e.
  * (floor(M*k/chunk_rows) + min(E, M*k)) * n_blocks.  Returns -1 on bad arguments. */
@@ -95,12 +104,19 @@ int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows);
  *                        then the partial ones by decreasing row count (largest first)
  *   ntasks s32 [1]       number of tasks written
  *   queue u32 [2]        reset to zero (the grouped GEMM's persistent work queue)
+ *   sorted_route_ids s32 [M*k]   optional (NULL: not written): the routes in expert order,
+ *                        sorted_route_ids[slot] = r for slot in [offsets[e], offsets[e+1])
+ *                        of e = topk_ids[r]; the order inside a segment is unspecified
+ *   route_slots s32 [M*k]        optional (only with sorted_route_ids): the inverse, -1 for
+ *                        ids outside [0, E)
  * chunk_rows in [1, 1024]; max_tasks must be >= moe_max_tasks(...) (else MOE_E_NOSPC).
- * One workgroup of 1024 threads; the order of tasks with equal row counts is unspecified. */
+ * One workgroup of 1024 threads; the order of tasks with equal row counts is unspecified.
+ * With sorted_route_ids set, do not also run moe_quant_sort_gather on the same cursors'
+ * segments expecting the same slots (it takes its own). */
 int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
                      int chunk_rows, int32_t* counts, int32_t* offsets, int32_t* cursors,
                      moe_task* tasks, int max_tasks, int32_t* ntasks, uint32_t* queue,
-                     moe_stream_t stream);
+                     int32_t* sorted_route_ids, int32_t* route_slots, moe_stream_t stream);
 
 /* ---- [FMF8] Baseline items 4-5 + Fusion 2 (QSG: quantise, sort, gather) ------------------
  * x bf16 [M][K], K a multiple of 128.  Per token and 128-wide block b:
@@ -170,6 +186,22 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                      int chunk_rows, uint32_t* queue, int epilogue,
                      const int32_t* sorted_route_ids, void* out, moe_stream_t stream);
 
+/* ---- [FMF8] Baseline items 5-6 with the gather done on load ------------------------------
+ * The grouped FP8 GEMM of moe_grouped_gemm (FP8_B128, MOE_EPI_ROUTE_F32) for chunk_rows in
+ * [65, 256] and K <= 8192, reading sorted row r from token sorted_route_ids[r] / k of the
+ * token-major codes x_q [M][K] and scales x_scales [K/128][M] (moe_route_quantize) instead
+ * of from a sorted copy:
+ *   rows[r_id][n] = sum_b x_scales[b][t] * w_scales[e][n/128][b] *
+ *                   sum_{kk in block b} e4m3(x_q[t][kk]) * e4m3(w[e][n][kk]),
+ * for every route r_id = sorted_route_ids[r] of a task's rows (t = r_id / k, e its expert),
+ * rows f32 [M*k][N].  tasks from moe_build_layout (n_tile 128, the same chunk_rows) with its
+ * sorted_route_ids.  One workgroup per task pair of one chunk (grid from max_tasks). */
+int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, int k, int K,
+                            const uint8_t* w, const float* w_scales, int E, int N,
+                            const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                            int chunk_rows, const int32_t* sorted_route_ids, float* rows,
+                            moe_stream_t stream);
+
 /* ---- [FMF8] Baseline items 2-6 fused: grouped FP8 GEMM straight from routed ids ------------
  * The small-batch GEMM of moe_forward: K = 2048, M*k <= 2048, N a multiple of 128, and E at
  * most about three times the CU count (one CU's share of the E*N/16 weight slices may touch at
@@ -202,8 +234,8 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
 
 /* Byte offset inside the workspace of one intermediate, for inspection in tests:
  * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
- * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (at route ids), 12 route_slots.
- * -1 on bad arguments. */
+ * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (at route ids), 12 route_slots,
+ * 13 x_q (token-major codes), 14 x_scales.  -1 on bad arguments. */
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
 
 /* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]
@@ -221,19 +253,23 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  * walk instead of the atomic queue (grouped GEMM forms that walk a queue). */
 #define MOE_FWD_GRAPH 1
 #define MOE_FWD_STATIC_GRID 2
-/* bit 2: always run the five staged kernels.  Without it, a small batch (the limits of
- * moe_grouped_gemm_routed, chunk_rows 16) runs three: route, the grouped GEMM straight from
- * the routed ids (layout, sort/gather and quantisation inside it; fp32 rows at route ids),
- * and the combine; the workspace then holds topk_ids, topk_weights and the GEMM rows (parts
- * 0, 1 and 11) but no counts, offsets, task list, sorted ids, a_q, a_scales or slots. */
+/* bit 2: always run the five staged kernels (route, layout, moe_quant_sort_gather, grouped
+ * GEMM, combine).  Without it:
+ *  - a small batch (the limits of moe_grouped_gemm_routed, chunk_rows 16) runs three:
+ *    route, the grouped GEMM straight from the routed ids (layout, sort/gather and
+ *    quantisation inside it; fp32 rows at route ids), and the combine; the workspace then
+ *    holds topk_ids, topk_weights and the GEMM rows (parts 0, 1 and 11) only;
+ *  - chunk_rows in [65, 256] (K <= 8192) runs four: moe_route_quantize, the layout with the
+ *    sorted route ids, moe_grouped_gemm_gather and the combine; the workspace then holds no
+ *    a_q or a_scales (parts 9 and 10) but the token-major x_q and x_scales (13, 14). */
 #define MOE_FWD_STAGED 4
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
 
-/* Number of kernels moe_forward_ex launches for these arguments: 3 (the small-batch path of
- * bit 2's description) or 5 (staged); MOE_E_INVAL for arguments moe_forward_ex rejects. */
+/* Number of kernels moe_forward_ex launches for these arguments: 3 or 4 (the paths of bit
+ * 2's description) or 5 (staged); MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
 /* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------

@@ -66,7 +66,7 @@ long long max_tasks_ll(int M, int k, int E, int n_blocks, int chunk_rows) {
 }
 
 // ---- workspace of moe_forward ----------------------------------------------------------
-constexpr int kWsParts = 13;
+constexpr int kWsParts = 15;
 struct WsLayout {
     size_t off[kWsParts];
     size_t total;
@@ -92,6 +92,8 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
         (size_t)(K / 128) * R * 4,  // 10 a_scales
         R * (size_t)N * 4,          // 11 GEMM rows, sorted order
         R * 4,                      // 12 route_slots
+        (size_t)M * K,              // 13 x_q (token-major codes)
+        (size_t)(K / 128) * M * 4,  // 14 x_scales
     };
     WsLayout L;
     size_t p = 0;
@@ -149,6 +151,23 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     const int Nb = a.N / 128;
     const int max_tasks = (int)max_tasks_ll(a.M, a.k, a.E, Nb, a.chunk);
     hipError_t e;
+    if (!(a.flags & MOE_FWD_STAGED) && gemm_fp8_tile_applies(a.K, a.chunk)) {
+        // larger batch: each token quantised once while it is routed; the layout sorts the
+        // routes; the tiled GEMM gathers each routed row from the token-major codes
+        uint8_t* x_q = reinterpret_cast<uint8_t*>(at(13));
+        float* x_s = reinterpret_cast<float*>(at(14));
+        if ((e = launch_route_quantize(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids, wts,
+                                       x_q, x_s, s)) != hipSuccess)
+            return e;
+        if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
+                               max_tasks, ntasks, queue, sorted, slots, s)) != hipSuccess)
+            return e;
+        if ((e = launch_gemm_fp8_tile_gather(x_q, x_s, a.M, a.k, a.K, a.w_q, a.w_scales, a.N,
+                                             tasks, ntasks, max_tasks, a.chunk, sorted, rows,
+                                             s)) != hipSuccess)
+            return e;
+        return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+    }
     if ((e = launch_route(a.logits, a.M, a.E, a.k, a.softcap, ids, wts, s)) != hipSuccess) return e;
     if (!(a.flags & MOE_FWD_STAGED) && forward_fused_applies(a.M, a.k, a.E, a.K, a.N, a.chunk)) {
         // small batch: layout, sort/gather and quantisation run inside the GEMM, whose fp32
@@ -159,7 +178,7 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
     }
     if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
-                           max_tasks, ntasks, queue, s)) != hipSuccess)
+                           max_tasks, ntasks, queue, nullptr, nullptr, s)) != hipSuccess)
         return e;
     if ((e = launch_qsg(a.x, a.M, a.K, ids, a.k, a.E, cursors, sorted, slots, a_q, a_s, s)) !=
         hipSuccess)
@@ -296,6 +315,20 @@ int moe_route(const float* logits, int M, int E, int k, float softcap, int32_t* 
                                    (hipStream_t)stream));
 }
 
+int moe_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k, int K,
+                       float softcap, int32_t* topk_ids, float* topk_weights, uint8_t* x_q,
+                       float* x_scales, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || K < 128 || K % 128 || (long long)M * K >= (1LL << 40))
+        return MOE_E_INVAL;
+    if (M > 0 && (!logits || !x || !topk_ids || !topk_weights || !x_q || !x_scales))
+        return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_route_quantize(logits, x, M, E, k, K, softcap, topk_ids,
+                                            topk_weights, x_q, x_scales, (hipStream_t)stream));
+}
+
 int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows) {
     if (!route_dims_ok(M, E, k) || n_blocks < 1 || chunk_rows < 1 || chunk_rows > 1024)
         return -1;
@@ -306,17 +339,19 @@ int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows) {
 int moe_build_layout(const int32_t* topk_ids, int M, int k, int E, int n_blocks,
                      int chunk_rows, int32_t* counts, int32_t* offsets, int32_t* cursors,
                      moe_task* tasks, int max_tasks, int32_t* ntasks, uint32_t* queue,
-                     moe_stream_t stream) {
+                     int32_t* sorted_route_ids, int32_t* route_slots, moe_stream_t stream) {
     const int need = moe_max_tasks(M, k, E, n_blocks, chunk_rows);
     if (need < 0) return MOE_E_INVAL;
     if ((M > 0 && !topk_ids) || !counts || !offsets || !cursors || !ntasks || !queue)
         return MOE_E_INVAL;
+    if (route_slots && !sorted_route_ids) return MOE_E_INVAL;
     if (need > 0 && !tasks) return MOE_E_INVAL;
     if (max_tasks < need) return MOE_E_NOSPC;
     int rc = check_device();
     if (rc) return rc;
     return hip_status(launch_layout(topk_ids, M, k, E, n_blocks, chunk_rows, counts, offsets,
                                     cursors, tasks, max_tasks, ntasks, queue,
+                                    M > 0 ? sorted_route_ids : nullptr, route_slots,
                                     (hipStream_t)stream));
 }
 
@@ -413,6 +448,23 @@ int moe_grouped_gemm_routed(const uint16_t* x, const int32_t* topk_ids, int M, i
     return hip_status(e);
 }
 
+int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, int k, int K,
+                            const uint8_t* w, const float* w_scales, int E, int N,
+                            const moe_task* tasks, const int32_t* ntasks, int max_tasks,
+                            int chunk_rows, const int32_t* sorted_route_ids, float* rows,
+                            moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
+        return MOE_E_INVAL;
+    if (!gemm_fp8_tile_applies(K, chunk_rows)) return MOE_E_INVAL;
+    if (!w || !w_scales || !ntasks || !rows || (max_tasks > 0 && !tasks)) return MOE_E_INVAL;
+    if (M > 0 && (!x_q || !x_scales || !sorted_route_ids)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_gemm_fp8_tile_gather(x_q, x_scales, M, k, K, w, w_scales, N, tasks,
+                                                  ntasks, max_tasks, chunk_rows,
+                                                  sorted_route_ids, rows, (hipStream_t)stream));
+}
+
 int moe_scatter(const float* rows, const int32_t* route_slots, const float* topk_weights,
                 const int32_t* topk_ids, int M, int k, int E, int N, uint16_t* out,
                 moe_stream_t stream) {
@@ -466,7 +518,9 @@ int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int f
     int rc = check_device();
     if (rc) return rc;
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
-    return !(flags & MOE_FWD_STAGED) && forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
+    if (flags & MOE_FWD_STAGED) return 5;
+    if (gemm_fp8_tile_applies(K, chunk)) return 4;
+    return forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
 
 int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
@@ -523,9 +577,9 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
     hipError_t e;
     if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
         (e = launch_layout(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu, mtu, nt,
-                           queue, s)) != hipSuccess ||
+                           queue, nullptr, nullptr, s)) != hipSuccess ||
         (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
-                           nt + 1, queue + 2, s)) != hipSuccess ||
+                           nt + 1, queue + 2, nullptr, nullptr, s)) != hipSuccess ||
         (e = launch_gather_bf16(x, M, H, ids, k, E, cursors, sorted, slots, rows, s)) !=
             hipSuccess ||
         (e = launch_gemm_bf16(rows, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s)) !=

@@ -66,17 +66,19 @@ struct TileStage {
     float sa[kWaves * 64];
 };
 
+// GATHER: sorted row r is token sorted_route_ids[r] / kr of the token-major codes `a` [M][K]
+// and scales [K/128][M] (rows = M), instead of row r of a sorted copy.
 // KBC: the number of k-blocks when known at compile time (0: K / 128 at run time).  With it the
 // k loop is fully unrolled and no DMA sits behind a run-time branch: the compiler's wait
 // tracking, which turns conservative where paths with different DMAs in flight meet, then
 // waits for exactly the stage each read needs.
-template <int BM, int EPI, int KBC>
+template <int BM, int EPI, int KBC, bool GATHER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
                           const uint8_t* __restrict__ w, const float* __restrict__ w_scales,
                           const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                           const int32_t* __restrict__ sorted_route_ids, void* __restrict__ out,
-                          int rows, int K, int N, int pairs, int chunks_per_xcd) {
+                          int rows, int K, int N, int pairs, int chunks_per_xcd, int kr) {
     using Cfg = TileCfg<BM>;
     constexpr int S = Cfg::kStages;
     __shared__ TileStage<BM> st0, st1, st2;     // st2 is used only with three stages
@@ -130,14 +132,19 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
         const int wr = nb0 * 128 + (r < np * 128 ? r : r - 128);
         srcW[i] = w + ((size_t)e * N + wr) * K + dc * 16;
     }
+    // source row of sorted row rb + i (i < rc)
+    auto src_row = [&](int i) __attribute__((always_inline)) -> size_t {
+        if (GATHER) return (size_t)(sorted_route_ids[rb + i] / kr);
+        return (size_t)(rb + i);
+    };
 #pragma unroll
     for (int i = 0; i < Cfg::kADma; ++i) {
         const int r = (wave + 8 * i) * 8 + dl;
         const int dc = (lane & 7) ^ ((r >> 1) & 7);
-        srcA[i] = a + (size_t)(rb + min(r, rc - 1)) * K + dc * 16;
+        srcA[i] = a + src_row(min(r, rc - 1)) * K + dc * 16;
     }
-    const uint8_t* srcPad = a + (size_t)(rb + rc - 1) * K;
-    const float* srcS = a_scales + rb + min(wave * 64 + lane, rc - 1);
+    const uint8_t* srcPad = a + src_row(rc - 1) * K;
+    const float* srcS = a_scales + src_row(min(wave * 64 + lane, rc - 1));
 
     auto issue = [&](auto bt, int kb) __attribute__((always_inline)) {
         TileStage<BM>& T = stage(bt);
@@ -263,11 +270,11 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
     }
 }
 
-template <int BM, int EPI>
+template <int BM, int EPI, bool GATHER>
 hipError_t launch_epi(const uint8_t* a, const float* a_scales, int rows, int K,
                       const uint8_t* w, const float* w_scales, int N, const moe_task* tasks,
                       const int32_t* ntasks, int max_tasks, const int32_t* sorted, void* out,
-                      hipStream_t s) {
+                      int kr, hipStream_t s) {
     const int Nb = N / 128;
     const int pairs = (Nb + 1) / 2;
     const int max_chunks = (max_tasks + Nb - 1) / Nb;
@@ -275,13 +282,13 @@ hipError_t launch_epi(const uint8_t* a, const float* a_scales, int rows, int K,
     const unsigned grid = (unsigned)(8 * cpx * pairs);
     const int4* t = reinterpret_cast<const int4*>(tasks);
     if (K == 2048)
-        hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 16>), dim3(grid), dim3(kThreads), 0, s,
-                           a, a_scales, w, w_scales, t, ntasks, sorted, out, rows, K, N, pairs,
-                           cpx);
+        hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 16, GATHER>), dim3(grid),
+                           dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted, out,
+                           rows, K, N, pairs, cpx, kr);
     else
-        hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 0>), dim3(grid), dim3(kThreads), 0, s,
-                           a, a_scales, w, w_scales, t, ntasks, sorted, out, rows, K, N, pairs,
-                           cpx);
+        hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 0, GATHER>), dim3(grid),
+                           dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted, out,
+                           rows, K, N, pairs, cpx, kr);
     return hipGetLastError();
 }
 
@@ -292,14 +299,17 @@ hipError_t launch_bm(const uint8_t* a, const float* a_scales, int rows, int K, c
                      void* out, hipStream_t s) {
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            return launch_epi<BM, MOE_EPI_STORE_BF16>(a, a_scales, rows, K, w, w_scales, N,
-                                                      tasks, ntasks, max_tasks, sorted, out, s);
+            return launch_epi<BM, MOE_EPI_STORE_BF16, false>(a, a_scales, rows, K, w, w_scales, N,
+                                                             tasks, ntasks, max_tasks, sorted,
+                                                             out, 1, s);
         case MOE_EPI_ROUTE_F32:
-            return launch_epi<BM, MOE_EPI_ROUTE_F32>(a, a_scales, rows, K, w, w_scales, N,
-                                                     tasks, ntasks, max_tasks, sorted, out, s);
+            return launch_epi<BM, MOE_EPI_ROUTE_F32, false>(a, a_scales, rows, K, w, w_scales, N,
+                                                            tasks, ntasks, max_tasks, sorted, out,
+                                                            1, s);
         default:
-            return launch_epi<BM, MOE_EPI_STORE_F32>(a, a_scales, rows, K, w, w_scales, N,
-                                                     tasks, ntasks, max_tasks, sorted, out, s);
+            return launch_epi<BM, MOE_EPI_STORE_F32, false>(a, a_scales, rows, K, w, w_scales, N,
+                                                            tasks, ntasks, max_tasks, sorted, out,
+                                                            1, s);
     }
 }
 
@@ -320,6 +330,20 @@ hipError_t launch_gemm_fp8_tile(const uint8_t* a, const float* a_scales, int row
                               epilogue, sorted, out, s);
     return launch_bm<256>(a, a_scales, rows, K, w, w_scales, N, tasks, ntasks, max_tasks,
                           epilogue, sorted, out, s);
+}
+
+hipError_t launch_gemm_fp8_tile_gather(const uint8_t* x_q, const float* x_scales, int M, int k,
+                                       int K, const uint8_t* w, const float* w_scales, int N,
+                                       const moe_task* tasks, const int32_t* ntasks,
+                                       int max_tasks, int chunk_rows, const int32_t* sorted,
+                                       float* rows_out, hipStream_t s) {
+    if (max_tasks <= 0) return hipSuccess;
+    if (chunk_rows <= 128)
+        return launch_epi<128, MOE_EPI_ROUTE_F32, true>(x_q, x_scales, M, K, w, w_scales, N,
+                                                        tasks, ntasks, max_tasks, sorted,
+                                                        rows_out, k, s);
+    return launch_epi<256, MOE_EPI_ROUTE_F32, true>(x_q, x_scales, M, K, w, w_scales, N, tasks,
+                                                    ntasks, max_tasks, sorted, rows_out, k, s);
 }
 
 }  // namespace moe

@@ -8,7 +8,10 @@
 // chunk_rows-row chunks of every expert first (expert order), then each expert's partial
 // chunk placed by a counting sort on its row count, largest first; every chunk is crossed
 // with the n_blocks weight panels (consecutive entries share the chunk).  The persistent
-// queue counter is reset here so the captured step needs no memset node.
+// queue counter is reset here so the captured step needs no memset node.  Optionally the
+// routes are also sorted by expert ([FMF8] Baseline item 5's slot assignment, here with LDS
+// atomics on per-expert cursors rather than global ones): sorted_route_ids[slot] = route and
+// route_slots[route] = slot, a slot's order inside its expert segment being arbitrary.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -40,30 +43,41 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& tot
 __global__ __launch_bounds__(kThreads) void layout_kernel(
     const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
-    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue) {
-    __shared__ int s_cnt[kThreads];
+    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue,
+    int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots) {
+    // one histogram per wave over its own contiguous range of routes: the LDS atomics of a
+    // busy expert are spread over 16 counters instead of queueing on one
+    __shared__ int s_hw[kWaves][kThreads];
     __shared__ int s_hist[kThreads];      // number of experts whose partial chunk has size s
     __shared__ int s_wsum[kWaves + 1];
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int span = (R + kWaves - 1) / kWaves;
+    const int r_lo = min(R, wave * span), r_hi = min(R, r_lo + span);
 
-    s_cnt[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s_hw[w][tid] = 0;
     s_hist[tid] = 0;
     __syncthreads();
 
-    for (int base = 0; base < R; base += 4 * kThreads) {
+    for (int base = r_lo; base < r_hi; base += 4 * 64) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int r = base + u * kThreads + tid;
-            v[u] = r < R ? ids[r] : -1;
+            const int r = base + u * 64 + lane;
+            v[u] = r < r_hi ? ids[r] : -1;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if ((unsigned)v[u] < (unsigned)E) atomicAdd(&s_cnt[v[u]], 1);
+            if ((unsigned)v[u] < (unsigned)E) atomicAdd(&s_hw[wave][v[u]], 1);
     }
     __syncthreads();
 
-    const int c = tid < E ? s_cnt[tid] : 0;
+    int c = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += s_hw[w][tid];
+    }
     const int full = c / chunk;
     const int tail = c - full * chunk;
     int total_rows, total_full;
@@ -84,6 +98,14 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
         counts[tid] = c;
         offsets[tid] = row0;
         cursors[tid] = row0;
+        // each wave's first slot inside the expert's segment (waves in route order)
+        int run = row0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int h = s_hw[w][tid];
+            s_hw[w][tid] = run;
+            run += h;
+        }
         if (tid == E - 1) offsets[E] = row0 + c;
         for (int i = 0; i < full; ++i) {
             const int p = full0 + i;
@@ -102,6 +124,28 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
         ntasks[0] = (total_full + total_tails) * n_blocks;
         queue[0] = 0u;
         queue[1] = 0u;
+    }
+    if (sorted_route_ids) {
+        __syncthreads();                                  // s_hw holds the wave cursors
+        for (int base = r_lo; base < r_hi; base += 4 * 64) {
+            int v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = base + u * 64 + lane;
+                v[u] = r < r_hi ? ids[r] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = base + u * 64 + lane;
+                if (r >= r_hi) continue;
+                int slot = -1;
+                if ((unsigned)v[u] < (unsigned)E) {
+                    slot = atomicAdd(&s_hw[wave][v[u]], 1);
+                    sorted_route_ids[slot] = r;
+                }
+                if (route_slots) route_slots[r] = slot;
+            }
+        }
     }
 }
 
@@ -133,10 +177,12 @@ __global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restr
 
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
                          int32_t* counts, int32_t* offsets, int32_t* cursors, moe_task* tasks,
-                         int max_tasks, int32_t* ntasks, uint32_t* queue, hipStream_t s) {
+                         int max_tasks, int32_t* ntasks, uint32_t* queue,
+                         int32_t* sorted_route_ids, int32_t* route_slots, hipStream_t s) {
     (void)max_tasks;  // capacity checked on the host against moe_max_tasks
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
-                       chunk_rows, counts, offsets, cursors, tasks, ntasks, queue);
+                       chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
+                       sorted_route_ids, route_slots);
     return hipGetLastError();
 }
 

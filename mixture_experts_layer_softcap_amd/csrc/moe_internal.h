@@ -18,9 +18,16 @@ const DeviceInfo& device_info();
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
                         int32_t* ids, float* weights, hipStream_t s);
 
+// route + per-token quantisation of x (token-major codes [M][K], scales [K/128][M])
+hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
+                                 int K, float softcap, int32_t* ids, float* weights,
+                                 uint8_t* x_q, float* x_scales, hipStream_t s);
+
+// sorted_route_ids / route_slots may be null (then the routes are not sorted)
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
                          int32_t* counts, int32_t* offsets, int32_t* cursors, moe_task* tasks,
-                         int max_tasks, int32_t* ntasks, uint32_t* queue, hipStream_t s);
+                         int max_tasks, int32_t* ntasks, uint32_t* queue,
+                         int32_t* sorted_route_ids, int32_t* route_slots, hipStream_t s);
 
 hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
                       int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,
@@ -55,6 +62,13 @@ hipError_t launch_gemm_fp8_tile(const uint8_t* a, const float* a_scales, int row
                                 const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                                 int chunk_rows, int epilogue, const int32_t* sorted, void* out,
                                 hipStream_t s);
+// the same with sorted row r read from token sorted[r] / k of x_q [M][K] (scales [K/128][M]);
+// fp32 rows written at route ids
+hipError_t launch_gemm_fp8_tile_gather(const uint8_t* x_q, const float* x_scales, int M, int k,
+                                       int K, const uint8_t* w, const float* w_scales, int N,
+                                       const moe_task* tasks, const int32_t* ntasks,
+                                       int max_tasks, int chunk_rows, const int32_t* sorted,
+                                       float* rows_out, hipStream_t s);
 
 // small-batch forward GEMM with the layout, sort/gather and quantisation folded in: weight
 // slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])

@@ -8,6 +8,12 @@
 // of a wave-wide maximum of the image (DPP row shifts and row broadcasts, no LDS), then one
 // ballot per register for the lowest-index holder of that maximum, which is retired.  tanh
 // and exp run only for the k winners, on lanes 0..k-1.
+//
+// With QUANT the wave also quantises its token's row of x once, with the rule of the
+// quantise-sort-gather stage ([FMF8] Baseline items 4-5: amax per 128-value block, scale =
+// amax/448, E4M3 of x times the reciprocal), into token-major codes [M][K] and scales
+// [K/128][M]: the grouped GEMM then gathers each routed row from there by its token instead
+// of reading a sorted copy of it (one copy per token, not one per route).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -36,14 +42,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-template <int VPL>
+template <int VPL, bool QUANT>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, float softcap,
-    int32_t* __restrict__ ids, float* __restrict__ weights) {
+    int32_t* __restrict__ ids, float* __restrict__ weights, const uint16_t* __restrict__ x,
+    int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
     if (t >= M) return;
     const float* row = logits + (size_t)t * E;
+    // the token's first 2048 values of x (four passes of 512) are requested before the
+    // routing work
+    constexpr int kPasses = 4;
+    uint4 xr[kPasses];
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+        xr[q] = make_uint4(0u, 0u, 0u, 0u);
+        if (QUANT && q * 512 + lane * 8 < K)
+            xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + q * 512 + lane * 8);
+    }
 
     float val[VPL];
     uint32_t ord[VPL];
@@ -97,27 +114,70 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         ids[(size_t)t * k + lane] = my_e;
         weights[(size_t)t * k + lane] = ex / sum;
     }
+    if (QUANT) {
+        // 512 values per pass: lane l holds values [8l, 8l+8) of the pass, so a 128-value
+        // block is an aligned group of 16 lanes (K is a multiple of 128: a group is wholly
+        // inside or outside the row); passes go in groups of four, loads first
+        for (int base = 0;;) {
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                const int k0 = base + q * 512 + lane * 8;
+                const bool valid = k0 < K;
+                const Quant8 qv = quantise8(xr[q], valid);
+                if (valid) {
+                    *reinterpret_cast<uint2*>(x_q + (size_t)t * K + k0) = qv.codes;
+                    if ((lane & 15) == 0) x_scales[(size_t)(k0 >> 7) * M + t] = qv.scale;
+                }
+            }
+            base += kPasses * 512;
+            if (base >= K) break;
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                const int k0 = base + q * 512 + lane * 8;
+                xr[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (k0 < K) xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0);
+            }
+        }
+    }
 }
 
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
-                      float* weights, hipStream_t s) {
+                      float* weights, const uint16_t* x, int K, uint8_t* x_q, float* x_scales,
+                      hipStream_t s) {
     const int grid = (M + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL(route_kernel<VPL>, dim3(grid), dim3(64 * kRouteWaves), 0, s, logits, M,
-                       E, k, softcap, ids, weights);
+    if (x_q)
+        hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid), dim3(64 * kRouteWaves), 0, s,
+                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
+    else
+        hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * kRouteWaves), 0, s,
+                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
     return hipGetLastError();
+}
+
+hipError_t launch_route_any(const float* logits, int M, int E, int k, float softcap,
+                            int32_t* ids, float* weights, const uint16_t* x, int K,
+                            uint8_t* x_q, float* x_scales, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (E <= 64) return launch_vpl<1>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+    if (E <= 128) return launch_vpl<2>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+    if (E <= 256) return launch_vpl<4>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+    if (E <= 512) return launch_vpl<8>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+    return launch_vpl<16>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                         float* weights, hipStream_t s) {
-    if (M == 0) return hipSuccess;
-    if (E <= 64) return launch_vpl<1>(logits, M, E, k, softcap, ids, weights, s);
-    if (E <= 128) return launch_vpl<2>(logits, M, E, k, softcap, ids, weights, s);
-    if (E <= 256) return launch_vpl<4>(logits, M, E, k, softcap, ids, weights, s);
-    if (E <= 512) return launch_vpl<8>(logits, M, E, k, softcap, ids, weights, s);
-    return launch_vpl<16>(logits, M, E, k, softcap, ids, weights, s);
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, nullptr, 0, nullptr,
+                            nullptr, s);
+}
+
+hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
+                                 int K, float softcap, int32_t* ids, float* weights,
+                                 uint8_t* x_q, float* x_scales, hipStream_t s) {
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
 }
 
 }  // namespace moe

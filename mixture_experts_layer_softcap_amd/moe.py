@@ -37,8 +37,9 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_device_check": (_I, []),
     "moe_route": (_I, [_P, _I, _I, _I, _F, _P, _P, _P]),
+    "moe_route_quantize": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "moe_max_tasks": (_I, [_I, _I, _I, _I, _I]),
-    "moe_build_layout": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "moe_build_layout": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "moe_quant_sort_gather": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_sort_gather_bf16": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -47,6 +48,8 @@ SIGNATURES = {
                               _P, _P, _P]),
     "moe_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_grouped_gemm_routed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
+    "moe_grouped_gemm_gather": (_I, [_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P,
+                                     _P]),
     "moe_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
@@ -115,6 +118,15 @@ def route(logits, k: int, softcap: float, topk_ids, topk_weights, stream=None):
           _stream(stream))
 
 
+def route_quantize(logits, x, k: int, softcap: float, topk_ids, topk_weights, x_q, x_scales,
+                   stream=None):
+    """moe_route plus the per-token E4M3 quantisation of x (moe_route_quantize)."""
+    M, E = logits.shape
+    K = x.shape[1]
+    _call("moe_route_quantize", _ptr(logits), _ptr(x), M, E, k, K, softcap, _ptr(topk_ids),
+          _ptr(topk_weights), _ptr(x_q), _ptr(x_scales), _stream(stream))
+
+
 def max_tasks(M: int, k: int, E: int, n_blocks: int, chunk_rows: int) -> int:
     v = lib().moe_max_tasks(M, k, E, n_blocks, chunk_rows)
     if v < 0:
@@ -123,11 +135,11 @@ def max_tasks(M: int, k: int, E: int, n_blocks: int, chunk_rows: int) -> int:
 
 
 def build_layout(topk_ids, E: int, n_blocks: int, chunk_rows: int, counts, offsets, cursors,
-                 tasks, ntasks, queue, stream=None):
+                 tasks, ntasks, queue, sorted_route_ids=None, route_slots=None, stream=None):
     M, k = topk_ids.shape
     _call("moe_build_layout", _ptr(topk_ids), M, k, E, n_blocks, chunk_rows, _ptr(counts),
           _ptr(offsets), _ptr(cursors), _ptr(tasks), tasks.shape[0], _ptr(ntasks), _ptr(queue),
-          _stream(stream))
+          _ptr(sorted_route_ids), _ptr(route_slots), _stream(stream))
 
 
 def quant_sort_gather(x, topk_ids, E: int, cursors, sorted_route_ids, a_q, a_scales,
@@ -157,9 +169,21 @@ def grouped_gemm(mode: int, a, a_scales, w, w_scales, tasks, ntasks, chunk_rows:
           _ptr(sorted_route_ids), _ptr(out), _stream(stream))
 
 
+def grouped_gemm_gather(x_q, x_scales, k: int, w_q, w_scales, tasks, ntasks, chunk_rows: int,
+                        sorted_route_ids, rows, stream=None):
+    """Grouped FP8 GEMM gathering routed rows from token-major codes (moe_grouped_gemm_gather);
+    rows f32 [M*k][N] at route ids."""
+    M, K = x_q.shape
+    E, N, _ = w_q.shape
+    _call("moe_grouped_gemm_gather", _ptr(x_q), _ptr(x_scales), M, k, K, _ptr(w_q),
+          _ptr(w_scales), E, N, _ptr(tasks), _ptr(ntasks), tasks.shape[0], chunk_rows,
+          _ptr(sorted_route_ids), _ptr(rows), _stream(stream))
+
+
 def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
                     flags: int = 0) -> int:
-    """Kernels moe_forward_ex launches for these arguments (3 small-batch path, 5 staged)."""
+    """Kernels moe_forward_ex launches for these arguments (3 or 4: the unstaged paths,
+    5 staged)."""
     n = lib().moe_forward_kernels(M, E, k, K, N, chunk_rows, flags)
     if n < 0:
         raise MoeError("moe_forward_kernels", n)

@@ -57,10 +57,10 @@ def test_workspace_queries(L):
     b = L.moe_forward_workspace_bytes(128, 256, 8, 2048, 512)
     R = 128 * 8
     assert b >= R * 2048 + R * 512 * 4 + 16 * 4 * R
-    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(13)]
+    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(15)]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < b
     assert L.moe_forward_workspace_bytes(128, 256, 8, 2000, 512) == 0   # K % 128
-    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 13) == -1
+    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 15) == -1
     fo = [L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, i) for i in range(14)]
     assert fo == sorted(fo) and all(o % 256 == 0 for o in fo)
     assert fo[-1] < L.moe_ffn_workspace_bytes(64, 8, 2, 512, 256)
@@ -82,9 +82,22 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert L.moe_route(P, 4, 8, 2, float("nan"), P, P, S) == INVAL    # NaN cap
     assert L.moe_route(P, -1, 8, 2, 30.0, P, P, S) == INVAL
     need = L.moe_max_tasks(16, 2, 8, 2, 4)
-    assert L.moe_build_layout(P, 16, 2, 8, 2, 4, P, P, P, P, need - 1, P, P, S) == NOSPC
-    assert L.moe_build_layout(P, 16, 2, 8, 2, 2000, P, P, P, P, 10 ** 6, P, P, S) == INVAL
-    assert L.moe_build_layout(P, 16, 2, 8, 2, 4, NULL, P, P, P, need, P, P, S) == INVAL
+    bl = L.moe_build_layout
+    assert bl(P, 16, 2, 8, 2, 4, P, P, P, P, need - 1, P, P, NULL, NULL, S) == NOSPC
+    assert bl(P, 16, 2, 8, 2, 2000, P, P, P, P, 10 ** 6, P, P, NULL, NULL, S) == INVAL
+    assert bl(P, 16, 2, 8, 2, 4, NULL, P, P, P, need, P, P, NULL, NULL, S) == INVAL
+    assert bl(P, 16, 2, 8, 2, 4, P, P, P, P, need, P, P, NULL, P, S) == INVAL  # slots alone
+    rq = L.moe_route_quantize
+    assert rq(P, P, 4, 8, 2, 200, 30.0, P, P, P, P, S) == INVAL      # K % 128
+    assert rq(P, NULL, 4, 8, 2, 256, 30.0, P, P, P, P, S) == INVAL   # null x
+    assert rq(P, P, 4, 8, 2, 256, 30.0, P, P, NULL, P, S) == INVAL   # null x_q
+    assert rq(P, P, 4, 8, 9, 256, 30.0, P, P, P, P, S) == INVAL      # k > E
+    gga = L.moe_grouped_gemm_gather
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 64, P, P, S) == INVAL     # chunk <= 64
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 257, P, P, S) == INVAL    # chunk > 256
+    assert gga(P, P, 4, 2, 8320, P, P, 8, 256, P, P, 8, 128, P, P, S) == INVAL   # K > 8192
+    assert gga(P, P, 4, 2, 256, P, P, 8, 200, P, P, 8, 128, P, P, S) == INVAL    # N % 128
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 128, NULL, P, S) == INVAL # sorted ids
     assert L.moe_quant_sort_gather(P, 4, 200, P, 2, 8, P, P, P, P, P, S) == INVAL  # K % 128
     assert L.moe_quant_sort_gather(P, 4, 256, NULL, 2, 8, P, P, P, P, P, S) == INVAL
     assert L.moe_quantize_weights(P, 2, 100, 256, P, P, S) == INVAL

@@ -81,6 +81,48 @@ def test_route_ties_and_signed_zero():
     assert (ids == np.arange(8)).all() and (w == np.float32(0.125)).all()
 
 
+@pytest.mark.parametrize("name", [TINY, QWEN, ZIPF1K])
+def test_route_quantize_matches_oracle(name):
+    # the route and, per token, the activation quantiser of the sort/gather stage: codes and
+    # scales bit-exact, token-major ([M][K] codes, [K/128][M] scales)
+    d = synth.workload_inputs(name, weights=False)
+    M, E, k, K = d["M"], d["E"], d["k"], d["K"]
+    ids, w = zeros((M, k), torch.int32), zeros((M, k), torch.float32)
+    x_q = torch.full((M, K), 0x55, dtype=torch.uint8, device=DEV)
+    x_s = torch.full((K // 128, M), -1.0, dtype=torch.float32, device=DEV)
+    moe.route_quantize(to_dev(d["logits"]), to_dev(d["x"]), k, CAP, ids, w, x_q, x_s)
+    sync()
+    rids, rw = orc.route(d["logits"], k, CAP)
+    np.testing.assert_array_equal(to_np(ids), rids)
+    np.testing.assert_allclose(to_np(w), rw, rtol=WEIGHT_RTOL, atol=0)
+    q, sc = orc.quant_act(d["x"])
+    np.testing.assert_array_equal(to_np(x_q), q)
+    np.testing.assert_array_equal(to_np(x_s).view(np.uint32), sc.T.copy().view(np.uint32))
+
+
+def test_route_quantize_edge_rows():
+    # K = 128 (one block: only the first 16 lanes of a pass hold data), a zero row, signed
+    # zeros and values that saturate; E = 16 with one token
+    g = np.random.default_rng(11)
+    for M, E, k, K in ((1, 16, 1, 128), (5, 64, 4, 640), (9, 300, 3, 1152)):
+        logits = g.standard_normal((M, E)).astype(np.float32)
+        xf = g.standard_normal((M, K)).astype(np.float32) * 3.0
+        xf[0, :128] = 0.0
+        xf[0, 1] = -0.0
+        if M > 1:
+            xf[1, 5] = 448.0 * 4
+        x = synth.bf16_bits(xf)
+        ids, w = zeros((M, k), torch.int32), zeros((M, k), torch.float32)
+        x_q = zeros((M, K), torch.uint8)
+        x_s = zeros((K // 128, M), torch.float32)
+        moe.route_quantize(to_dev(logits), to_dev(x), k, CAP, ids, w, x_q, x_s)
+        sync()
+        q, sc = orc.quant_act(x)
+        np.testing.assert_array_equal(to_np(x_q), q)
+        np.testing.assert_array_equal(to_np(x_s).view(np.uint32), sc.T.copy().view(np.uint32))
+        np.testing.assert_array_equal(to_np(ids), orc.route(logits, k, CAP)[0])
+
+
 # ---- stage 2: layout -------------------------------------------------------------------
 
 def gpu_layout(ids, E, n_blocks, chunk):
@@ -126,6 +168,37 @@ def test_layout_workloads(name, chunk):
     d = synth.workload_inputs(name, weights=False)
     ids, _ = orc.route(d["logits"], d["k"], CAP)
     check_layout(ids, d["E"], d["N"] // 128, chunk)
+
+
+@pytest.mark.parametrize("name,chunk", [(TINY, 128), (QWEN, 128), (ZIPF1K, 128), (ZIPF4K, 256)])
+def test_layout_sorted_routes(name, chunk):
+    # the layout's own sort: every segment holds exactly its expert's routes (order free),
+    # route_slots is the inverse permutation; counts/offsets/tasks as without the sort
+    d = synth.workload_inputs(name, weights=False)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    E = d["E"]
+    M, k = ids.shape
+    nb = d["N"] // 128
+    mt = moe.max_tasks(M, k, E, nb, chunk)
+    counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
+    tasks = zeros((mt, 4), torch.int32)
+    ntasks, queue = zeros(1, torch.int32), zeros(2, torch.int32)
+    srt = torch.full((M * k,), -5, dtype=torch.int32, device=DEV)
+    slots = torch.full((M * k,), -5, dtype=torch.int32, device=DEV)
+    moe.build_layout(to_dev(ids), E, nb, chunk, counts, offsets, cursors, tasks, ntasks, queue,
+                     sorted_route_ids=srt, route_slots=slots)
+    sync()
+    rcounts, roffsets = orc.layout(ids, E)
+    np.testing.assert_array_equal(to_np(offsets), roffsets)
+    s_ids, sl = to_np(srt), to_np(slots)
+    r_ids, _, _ = orc.sort_gather(ids, roffsets, np.zeros((M, 128), np.uint8),
+                                  np.zeros((M, 1), np.float32))
+    perm = canonical_segments(s_ids, roffsets)
+    np.testing.assert_array_equal(s_ids[perm], r_ids)
+    np.testing.assert_array_equal(s_ids[sl], np.arange(M * k))
+    n = int(to_np(ntasks)[0])
+    ref_tasks = orc.tasks(rcounts, roffsets, nb, chunk)
+    assert n == len(ref_tasks)
 
 
 def test_layout_edge_cases():
@@ -318,6 +391,68 @@ def test_gemm_tiled_multi_chunk_epilogues(chunk):
     perm = g.permutation(rows).astype(np.int32)     # a route id per sorted row
     rt = gpu_gemm(a_q, sa, w_q, sb, offsets, chunk, moe.MOE_EPI_ROUTE_F32, sorted_ids=perm)
     np.testing.assert_array_equal(rt[perm], ref)
+
+
+def gpu_gemm_gather(x_q, x_s, ids, w_q, w_s, chunk):
+    """moe_build_layout (sorted) + moe_grouped_gemm_gather on device; rows at route ids."""
+    M, k = ids.shape
+    E, N, K = w_q.shape
+    nb = N // 128
+    mt = moe.max_tasks(M, k, E, nb, chunk)
+    counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
+    tasks = zeros((mt, 4), torch.int32)
+    ntasks, queue = zeros(1, torch.int32), zeros(2, torch.int32)
+    srt = zeros(M * k, torch.int32)
+    ids_d = to_dev(ids)
+    moe.build_layout(ids_d, E, nb, chunk, counts, offsets, cursors, tasks, ntasks, queue,
+                     sorted_route_ids=srt)
+    rows = torch.full((M * k, N), -3.0, dtype=torch.float32, device=DEV)
+    moe.grouped_gemm_gather(to_dev(x_q), to_dev(x_s), k, to_dev(w_q), to_dev(w_s), tasks, ntasks,
+                            chunk, srt, rows)
+    sync()
+    return to_np(rows)
+
+
+@pytest.mark.parametrize("chunk", [96, 128, 256])
+def test_gemm_gather_integer_exact(chunk):
+    # token-major integer codes with power-of-two scales: the GEMM is exact in fp32; experts of
+    # 0 .. 300 routes exercise full, ragged and one-row tiles
+    g = np.random.default_rng(chunk)
+    M, k, E, N, K = 160, 3, 5, 384, 640
+    bias = np.array([3.0, 2.0, 0.0, -9.0, 1.0], np.float32)
+    logits = (g.standard_normal((M, E)) + bias).astype(np.float32)
+    ids, _ = orc.route(logits, k, CAP)
+    Ai = g.integers(-4, 5, (M, K))
+    Wi = g.integers(-4, 5, (E, N, K))
+    sa = np.exp2(g.integers(-1, 2, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(g.integers(-1, 2, (E, N // 128, K // 128))).astype(np.float32)
+    counts, offsets = orc.layout(ids, E)
+    r_ids, a_q, a_s = orc.sort_gather(ids, offsets, int_codes(Ai), sa)
+    C = orc.gemm_fp8(a_q, a_s, int_codes(Wi), sb, offsets).astype(np.float32)
+    got = gpu_gemm_gather(int_codes(Ai), sa.T.copy(), ids, int_codes(Wi), sb, chunk)
+    np.testing.assert_array_equal(got[r_ids], C)
+
+
+@pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
+def test_gemm_gather_workload_rows(name):
+    # full-size skewed layers; fp32 rows against the exact oracle rows of sampled routes
+    d = workload(name)
+    ids, _ = orc.route(d["logits"], d["k"], CAP)
+    q, sc = orc.quant_act(d["x"])
+    got = gpu_gemm_gather(q, sc.T.copy(), ids, d["w_q"], d["w_s"], 128)
+    counts, offsets = orc.layout(ids, d["E"])
+    g = np.random.default_rng(1)
+    busiest = int(np.argmax(counts))
+    on_busy = np.nonzero((ids == busiest).any(1))[0]
+    toks = np.unique(np.concatenate([[0, d["M"] - 1], g.choice(d["M"], 40, replace=False),
+                                     on_busy[:3], on_busy[-3:]]))
+    k = d["k"]
+    sub_ids = ids[toks]
+    s_counts, s_offsets = orc.layout(sub_ids, d["E"])
+    r_ids, a_q, a_s = orc.sort_gather(sub_ids, s_offsets, q[toks], sc[toks])
+    C = orc.gemm_fp8(a_q, a_s, d["w_q"], d["w_s"], s_offsets)
+    full = toks[r_ids // k] * k + r_ids % k          # route ids of the whole layer
+    assert_gemm_f32_close(got[full], C, name)
 
 
 def test_gemm_random_store_modes():
