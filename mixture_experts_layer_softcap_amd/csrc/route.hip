@@ -20,7 +20,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteWaves = 4;
+constexpr int kRouteWaves = 4;   // tokens (waves) per workgroup at most
 
 // monotone 32-bit image of a logit (the high word of route_key)
 __device__ __forceinline__ uint32_t logit_ord(float v) { return (uint32_t)(route_key(v, 0) >> 32); }
@@ -42,13 +42,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// One wave per token; blockDim.x / 64 tokens per workgroup (one while the batch is smaller than
+// four per CU, so small batches spread over the CUs).
 template <int VPL, bool QUANT>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, float softcap,
     int32_t* __restrict__ ids, float* __restrict__ weights, const uint16_t* __restrict__ x,
     int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+    const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= M) return;
     const float* row = logits + (size_t)t * E;
     // the token's first 2048 values of x (four passes of 512) are requested before the
@@ -145,12 +147,13 @@ template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                       float* weights, const uint16_t* x, int K, uint8_t* x_q, float* x_scales,
                       hipStream_t s) {
-    const int grid = (M + kRouteWaves - 1) / kRouteWaves;
+    const int per = M >= kRouteWaves * device_info().cu_count ? kRouteWaves : 1;
+    const int grid = (M + per - 1) / per;
     if (x_q)
-        hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid), dim3(64 * kRouteWaves), 0, s,
+        hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid), dim3(64 * per), 0, s,
                            logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
     else
-        hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * kRouteWaves), 0, s,
+        hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * per), 0, s,
                            logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
     return hipGetLastError();
 }
@@ -159,11 +162,13 @@ hipError_t launch_route_any(const float* logits, int M, int E, int k, float soft
                             int32_t* ids, float* weights, const uint16_t* x, int K,
                             uint8_t* x_q, float* x_scales, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (E <= 64) return launch_vpl<1>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
-    if (E <= 128) return launch_vpl<2>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
-    if (E <= 256) return launch_vpl<4>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
-    if (E <= 512) return launch_vpl<8>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
-    return launch_vpl<16>(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s
+    if (E <= 64) return launch_vpl<1>(MOE_ROUTE_ARGS);
+    if (E <= 128) return launch_vpl<2>(MOE_ROUTE_ARGS);
+    if (E <= 256) return launch_vpl<4>(MOE_ROUTE_ARGS);
+    if (E <= 512) return launch_vpl<8>(MOE_ROUTE_ARGS);
+    return launch_vpl<16>(MOE_ROUTE_ARGS);
+#undef MOE_ROUTE_ARGS
 }
 
 }  // namespace

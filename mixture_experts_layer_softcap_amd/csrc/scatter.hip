@@ -2,8 +2,8 @@
 // ([FMF8] "Baseline: 7 kernels" item 7 and Fusion 1: token = route_id / TOPK,
 // weight = topk_weights[token, route_id % TOPK], output[token] += weight * row).
 //
-// The GEMM writes its fp32 rows with plain 16-byte stores (in sorted order, or at the route
-// id), and the scatter-add becomes a gather-sum per token:
+// The GEMM writes its fp32 rows with plain stores (in sorted order, or at the route id), and
+// the scatter-add becomes a gather-sum per token:
 // out[t] = bf16(sum_j w[t][j] * row(t*k+j)), summed in fp32 in j order.  No float atomics,
 // no zero-initialised accumulator, and the result does not depend on the order of rows
 // inside an expert segment.
@@ -21,17 +21,20 @@ constexpr int kThreads = 256;
 // terms skipped.
 constexpr int kGroup = 8;
 
-template <bool SLOTS>
+// CPT output columns per thread (4, 2 or 1): small batches use narrower threads so the grid
+// covers every CU (a CU's requests in flight, not the bytes, bound this kernel).
+template <bool SLOTS, int CPT>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const float* __restrict__ rows, const int32_t* __restrict__ route_slots,
     const float* __restrict__ weights, const int32_t* __restrict__ ids, int M, int k, int E,
     int N, uint16_t* __restrict__ out) {
-    const int quads = N >> 2;
+    typedef float vec __attribute__((ext_vector_type(CPT)));
+    const int groups = N / CPT;
     const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= (size_t)M * quads) return;
-    const int t = (int)(idx / quads);
-    const int n = (int)(idx % quads) * 4;
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (idx >= (size_t)M * groups) return;
+    const int t = (int)(idx / groups);
+    const int n = (int)(idx % groups) * CPT;
+    vec acc = (vec)0.0f;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         int e[kGroup];
         float wv[kGroup];
@@ -47,24 +50,46 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
                 row[u] = sl < 0 ? 0 : (size_t)sl;
             }
         }
-        float4 v[kGroup];
+        vec v[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) v[u] = *reinterpret_cast<const vec*>(rows + row[u] * N + n);
 #pragma unroll
         for (int u = 0; u < kGroup; ++u)
-            v[u] = *reinterpret_cast<const float4*>(rows + row[u] * N + n);
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            if (j0 + u < k && (unsigned)e[u] < (unsigned)E) {
-                acc.x += wv[u] * v[u].x;
-                acc.y += wv[u] * v[u].y;
-                acc.z += wv[u] * v[u].z;
-                acc.w += wv[u] * v[u].w;
-            }
-        }
+            if (j0 + u < k && (unsigned)e[u] < (unsigned)E) acc += wv[u] * v[u];
     }
-    uint2 o;
-    o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
-    o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
-    *reinterpret_cast<uint2*>(out + (size_t)t * N + n) = o;
+    if constexpr (CPT == 4) {
+        uint2 o;
+        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(out + (size_t)t * N + n) = o;
+    } else if constexpr (CPT == 2) {
+        *reinterpret_cast<uint32_t*>(out + (size_t)t * N + n) =
+            f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    } else {
+        out[(size_t)t * N + n] = (uint16_t)f32_to_bf16(acc[0]);
+    }
+}
+
+template <bool SLOTS>
+hipError_t launch_slots(const float* rows, const int32_t* route_slots, const float* weights,
+                        const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
+                        hipStream_t s) {
+    // widest threads that still give one workgroup per CU
+    const size_t cus = (size_t)device_info().cu_count;
+    int cpt = 4;
+    while (cpt > 1 && (N % cpt || (size_t)M * (N / cpt) < cus * kThreads)) cpt >>= 1;
+    const size_t work = (size_t)M * (N / cpt);
+    const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
+    if (cpt == 4)
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, 4>), dim3(grid), dim3(kThreads), 0, s, rows,
+                           route_slots, weights, ids, M, k, E, N, out);
+    else if (cpt == 2)
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, 2>), dim3(grid), dim3(kThreads), 0, s, rows,
+                           route_slots, weights, ids, M, k, E, N, out);
+    else
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, 1>), dim3(grid), dim3(kThreads), 0, s, rows,
+                           route_slots, weights, ids, M, k, E, N, out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -72,16 +97,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
                           hipStream_t s) {
-    const size_t work = (size_t)M * (N / 4);
-    if (work == 0) return hipSuccess;
-    const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
+    if ((size_t)M * N == 0) return hipSuccess;
     if (route_slots)
-        hipLaunchKernelGGL(scatter_kernel<true>, dim3(grid), dim3(kThreads), 0, s, rows,
-                           route_slots, weights, ids, M, k, E, N, out);
-    else
-        hipLaunchKernelGGL(scatter_kernel<false>, dim3(grid), dim3(kThreads), 0, s, rows,
-                           route_slots, weights, ids, M, k, E, N, out);
-    return hipGetLastError();
+        return launch_slots<true>(rows, route_slots, weights, ids, M, k, E, N, out, s);
+    return launch_slots<false>(rows, route_slots, weights, ids, M, k, E, N, out, s);
 }
 
 }  // namespace moe
