@@ -339,7 +339,8 @@ def main():
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if K <= 8192 else 64))
     nkern = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags)
-    fused, gather = nkern == 3, nkern == 4
+    fused = nkern == 3
+    gather = not args.staged and 64 < chunk <= 256 and K <= 8192
     rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
     if gather:
         # the step's tiled GEMM on what the last step left in the workspace: token-major codes
@@ -409,8 +410,8 @@ def main():
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
                    "path": ("3 kernels: route, grouped GEMM from the routed ids, combine" if fused
-                            else "4 kernels: route+quantise, layout+sort, gathering grouped "
-                                 "GEMM, combine" if gather
+                            else "5 kernels: route+quantise, count, sort+layout, gathering "
+                                 "grouped GEMM, combine" if gather
                             else "5 kernels: route, layout, QSG, grouped GEMM, combine"),
                    "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
                                       else "contiguous ranges, per-wave pull"

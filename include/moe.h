@@ -235,7 +235,7 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
 /* Byte offset inside the workspace of one intermediate, for inspection in tests:
  * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
  * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (at route ids), 12 route_slots,
- * 13 x_q (token-major codes), 14 x_scales.  -1 on bad arguments. */
+ * 13 x_q (token-major codes), 14 x_scales, 15 slot cursors.  -1 on bad arguments. */
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
 
 /* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]
@@ -259,17 +259,19 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  *    route, the grouped GEMM straight from the routed ids (layout, sort/gather and
  *    quantisation inside it; fp32 rows at route ids), and the combine; the workspace then
  *    holds topk_ids, topk_weights and the GEMM rows (parts 0, 1 and 11) only;
- *  - chunk_rows in [65, 256] (K <= 8192) runs four: moe_route_quantize, the layout with the
- *    sorted route ids, moe_grouped_gemm_gather and the combine; the workspace then holds no
- *    a_q or a_scales (parts 9 and 10) but the token-major x_q and x_scales (13, 14). */
+ *  - chunk_rows in [65, 256] (K <= 8192) runs five: moe_route_quantize, the layout with the
+ *    sorted route ids over many workgroups (a count kernel and a sort kernel), the
+ *    moe_grouped_gemm_gather GEMM and the combine; the workspace then holds no a_q, a_scales
+ *    or route_slots (parts 9, 10, 12) but the token-major x_q and x_scales (13, 14) and the
+ *    sort's slot cursors (15). */
 #define MOE_FWD_STAGED 4
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
 
-/* Number of kernels moe_forward_ex launches for these arguments: 3 or 4 (the paths of bit
- * 2's description) or 5 (staged); MOE_E_INVAL for arguments moe_forward_ex rejects. */
+/* Number of kernels moe_forward_ex launches for these arguments: 3 (small batch) or 5 (the
+ * gathering path or the staged one); MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
 /* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------

@@ -66,7 +66,7 @@ long long max_tasks_ll(int M, int k, int E, int n_blocks, int chunk_rows) {
 }
 
 // ---- workspace of moe_forward ----------------------------------------------------------
-constexpr int kWsParts = 15;
+constexpr int kWsParts = 16;
 struct WsLayout {
     size_t off[kWsParts];
     size_t total;
@@ -94,6 +94,7 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
         R * 4,                      // 12 route_slots
         (size_t)M * K,              // 13 x_q (token-major codes)
         (size_t)(K / 128) * M * 4,  // 14 x_scales
+        (size_t)E * 4,              // 15 per-expert slot cursors of the wide layout
     };
     WsLayout L;
     size_t p = 0;
@@ -156,11 +157,13 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         // routes; the tiled GEMM gathers each routed row from the token-major codes
         uint8_t* x_q = reinterpret_cast<uint8_t*>(at(13));
         float* x_s = reinterpret_cast<float*>(at(14));
-        if ((e = launch_route_quantize(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids, wts,
-                                       x_q, x_s, s)) != hipSuccess)
+        int32_t* rel = reinterpret_cast<int32_t*>(at(15));
+        if ((e = launch_route_quantize_zero(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids,
+                                            wts, x_q, x_s, counts, rel, a.E, s)) != hipSuccess)
             return e;
-        if ((e = launch_layout(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets, cursors, tasks,
-                               max_tasks, ntasks, queue, sorted, slots, s)) != hipSuccess)
+        if ((e = launch_layout_sorted_wide(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets,
+                                           cursors, tasks, ntasks, queue, rel, sorted, s)) !=
+            hipSuccess)
             return e;
         if ((e = launch_gemm_fp8_tile_gather(x_q, x_s, a.M, a.k, a.K, a.w_q, a.w_scales, a.N,
                                              tasks, ntasks, max_tasks, a.chunk, sorted, rows,
@@ -519,7 +522,7 @@ int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int f
     if (rc) return rc;
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
     if (flags & MOE_FWD_STAGED) return 5;
-    if (gemm_fp8_tile_applies(K, chunk)) return 4;
+    if (gemm_fp8_tile_applies(K, chunk)) return 5;
     return forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
 

@@ -40,6 +40,52 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& tot
     return excl;
 }
 
+// The task list of expert counts c (thread e holds c_e and its exclusive prefix row0): full
+// chunk_rows-row chunks first (expert order), then the partial chunks by a counting sort on
+// their row count, largest first, each crossed with the n_blocks panels; also offsets[E+1],
+// cursors = offsets, ntasks, and the queue reset.  Every thread of the workgroup calls it.
+__device__ void write_tasks(int c, int row0, int E, int n_blocks, int chunk,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
+                            moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks,
+                            uint32_t* __restrict__ queue, int* s_hist, int* s_wsum) {
+    const int tid = threadIdx.x;
+    const int full = c / chunk;
+    const int tail = c - full * chunk;
+    int total_full;
+    const int full0 = block_exclusive_scan(full, s_wsum, total_full);
+    if (tail > 0) atomicAdd(&s_hist[tail], 1);
+    __syncthreads();
+    // descending scan over partial-chunk sizes: thread i looks at size chunk-1-i
+    const int size = chunk - 1 - tid;
+    const int h = size >= 1 ? s_hist[size] : 0;
+    int total_tails;
+    const int larger = block_exclusive_scan(h, s_wsum, total_tails);
+    if (size >= 1) s_hist[size] = larger;                 // first position of size `size`
+    __syncthreads();
+    if (tid < E) {
+        offsets[tid] = row0;
+        cursors[tid] = row0;
+        if (tid == E - 1) offsets[E] = row0 + c;
+        for (int i = 0; i < full; ++i) {
+            const int p = full0 + i;
+            for (int nb = 0; nb < n_blocks; ++nb)
+                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
+                    make_int4(tid, row0 + i * chunk, chunk, nb);
+        }
+        if (tail > 0) {
+            const int p = total_full + atomicAdd(&s_hist[tail], 1);
+            for (int nb = 0; nb < n_blocks; ++nb)
+                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
+                    make_int4(tid, row0 + full * chunk, tail, nb);
+        }
+    }
+    if (tid == 0) {
+        ntasks[0] = (total_full + total_tails) * n_blocks;
+        queue[0] = 0u;
+        queue[1] = 0u;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void layout_kernel(
     const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
@@ -60,7 +106,18 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
     s_hist[tid] = 0;
     __syncthreads();
 
-    for (int base = r_lo; base < r_hi; base += 4 * 64) {
+    // a wave's ids stay in registers for the sort (kHeld per lane; a larger range is read again)
+    constexpr int kHeld = 32;
+    int held[kHeld];
+#pragma unroll
+    for (int u = 0; u < kHeld; ++u) {
+        const int r = r_lo + u * 64 + lane;
+        held[u] = r < r_hi ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kHeld; ++u)
+        if ((unsigned)held[u] < (unsigned)E) atomicAdd(&s_hw[wave][held[u]], 1);
+    for (int base = r_lo + kHeld * 64; base < r_hi; base += 4 * 64) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -78,26 +135,12 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) c += s_hw[w][tid];
     }
-    const int full = c / chunk;
-    const int tail = c - full * chunk;
-    int total_rows, total_full;
+    int total_rows;
     const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
-    const int full0 = block_exclusive_scan(full, s_wsum, total_full);
-
-    if (tail > 0) atomicAdd(&s_hist[tail], 1);
-    __syncthreads();
-    // descending scan over partial-chunk sizes: thread i looks at size chunk-1-i
-    const int size = chunk - 1 - tid;
-    const int h = size >= 1 ? s_hist[size] : 0;
-    int total_tails;
-    const int larger = block_exclusive_scan(h, s_wsum, total_tails);
-    if (size >= 1) s_hist[size] = larger;                 // first position of size `size`
-    __syncthreads();
-
+    write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
+                s_wsum);
     if (tid < E) {
         counts[tid] = c;
-        offsets[tid] = row0;
-        cursors[tid] = row0;
         // each wave's first slot inside the expert's segment (waves in route order)
         int run = row0;
 #pragma unroll
@@ -106,28 +149,21 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
             s_hw[w][tid] = run;
             run += h;
         }
-        if (tid == E - 1) offsets[E] = row0 + c;
-        for (int i = 0; i < full; ++i) {
-            const int p = full0 + i;
-            for (int nb = 0; nb < n_blocks; ++nb)
-                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
-                    make_int4(tid, row0 + i * chunk, chunk, nb);
-        }
-        if (tail > 0) {
-            const int p = total_full + atomicAdd(&s_hist[tail], 1);
-            for (int nb = 0; nb < n_blocks; ++nb)
-                *reinterpret_cast<int4*>(&tasks[(size_t)p * n_blocks + nb]) =
-                    make_int4(tid, row0 + full * chunk, tail, nb);
-        }
-    }
-    if (tid == 0) {
-        ntasks[0] = (total_full + total_tails) * n_blocks;
-        queue[0] = 0u;
-        queue[1] = 0u;
     }
     if (sorted_route_ids) {
         __syncthreads();                                  // s_hw holds the wave cursors
-        for (int base = r_lo; base < r_hi; base += 4 * 64) {
+        auto place = [&](int r, int e) __attribute__((always_inline)) {
+            if (r >= r_hi) return;
+            int slot = -1;
+            if ((unsigned)e < (unsigned)E) {
+                slot = atomicAdd(&s_hw[wave][e], 1);
+                sorted_route_ids[slot] = r;
+            }
+            if (route_slots) route_slots[r] = slot;
+        };
+#pragma unroll
+        for (int u = 0; u < kHeld; ++u) place(r_lo + u * 64 + lane, held[u]);
+        for (int base = r_lo + kHeld * 64; base < r_hi; base += 4 * 64) {
             int v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -135,16 +171,7 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
                 v[u] = r < r_hi ? ids[r] : -1;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = base + u * 64 + lane;
-                if (r >= r_hi) continue;
-                int slot = -1;
-                if ((unsigned)v[u] < (unsigned)E) {
-                    slot = atomicAdd(&s_hw[wave][v[u]], 1);
-                    sorted_route_ids[slot] = r;
-                }
-                if (route_slots) route_slots[r] = slot;
-            }
+            for (int u = 0; u < 4; ++u) place(base + u * 64 + lane, v[u]);
         }
     }
 }
@@ -173,6 +200,56 @@ __global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restr
     }
 }
 
+// ---- the same layout over many workgroups (the forward's larger batches) ------------------
+// A single workgroup is bound by its own CU's requests in flight; here every workgroup takes
+// kThreads routes, one per thread.  count_kernel adds each chunk's LDS histogram into counts
+// (zeroed by the preceding route kernel); sort_layout_kernel recomputes the offsets in every
+// workgroup from the counts, workgroup 0 writes offsets, cursors, the task list, ntasks and
+// the queue reset as layout_kernel does, and each chunk reserves its slots inside every expert
+// segment with one returning atomic per expert on rel (zeroed likewise), then places its own
+// routes by their LDS ranks.  The chunks' order inside a segment follows their atomics.
+
+__global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restrict__ ids, int R,
+                                                         int E, int32_t* __restrict__ counts) {
+    __shared__ int s_h[kThreads];
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x * kThreads + tid;
+    const int e = r < R ? ids[r] : -1;
+    s_h[tid] = 0;
+    __syncthreads();
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_h[e], 1);
+    __syncthreads();
+    if (tid < E && s_h[tid] > 0) atomicAdd(&counts[tid], s_h[tid]);
+}
+
+__global__ __launch_bounds__(kThreads) void sort_layout_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ cursors, moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks,
+    uint32_t* __restrict__ queue, int32_t* __restrict__ rel,
+    int32_t* __restrict__ sorted_route_ids) {
+    __shared__ int s_h[kThreads];
+    __shared__ int s_base[kThreads];
+    __shared__ int s_hist[kThreads];
+    __shared__ int s_wsum[kWaves + 1];
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x * kThreads + tid;
+    const int e = r < R ? ids[r] : -1;
+    const int c = tid < E ? counts[tid] : 0;
+    s_h[tid] = 0;
+    s_hist[tid] = 0;
+    __syncthreads();
+    const int rank = (unsigned)e < (unsigned)E ? atomicAdd(&s_h[e], 1) : -1;
+    int total_rows;
+    const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
+    if (blockIdx.x == 0)
+        write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
+                    s_wsum);
+    if (tid < E && s_h[tid] > 0) s_base[tid] = row0 + atomicAdd(&rel[tid], s_h[tid]);
+    __syncthreads();
+    if (rank >= 0) sorted_route_ids[s_base[e] + rank] = r;
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
@@ -183,6 +260,23 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
                        chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
                        sorted_route_ids, route_slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, int n_blocks,
+                                     int chunk_rows, int32_t* counts, int32_t* offsets,
+                                     int32_t* cursors, moe_task* tasks, int32_t* ntasks,
+                                     uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
+                                     hipStream_t s) {
+    const int R = M * k;
+    if (R == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((R + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(count_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sort_layout_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
+                       n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue, rel,
+                       sorted_route_ids);
     return hipGetLastError();
 }
 

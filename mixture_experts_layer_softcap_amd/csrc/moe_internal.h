@@ -23,6 +23,19 @@ hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, 
                                  int K, float softcap, int32_t* ids, float* weights,
                                  uint8_t* x_q, float* x_scales, hipStream_t s);
 
+// the same, also zeroing zero0[0..zero_n) and zero1[0..zero_n) (scratch of the wide layout)
+hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
+                                      int k, int K, float softcap, int32_t* ids, float* weights,
+                                      uint8_t* x_q, float* x_scales, int32_t* zero0,
+                                      int32_t* zero1, int zero_n, hipStream_t s);
+
+// the layout with the sorted route ids over many workgroups: counts and rel [E] must be zero
+hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, int n_blocks,
+                                     int chunk_rows, int32_t* counts, int32_t* offsets,
+                                     int32_t* cursors, moe_task* tasks, int32_t* ntasks,
+                                     uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
+                                     hipStream_t s);
+
 // sorted_route_ids / route_slots may be null (then the routes are not sorted)
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
                          int32_t* counts, int32_t* offsets, int32_t* cursors, moe_task* tasks,

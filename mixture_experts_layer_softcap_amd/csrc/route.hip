@@ -48,8 +48,16 @@ template <int VPL, bool QUANT>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, float softcap,
     int32_t* __restrict__ ids, float* __restrict__ weights, const uint16_t* __restrict__ x,
-    int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales) {
+    int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales, int32_t* __restrict__ zero0,
+    int32_t* __restrict__ zero1, int zero_n) {
     const int lane = threadIdx.x & 63;
+    // scratch the next kernels accumulate into (per-expert counts and cursors)
+    if (zero0 && blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < zero_n; i += blockDim.x) {
+            zero0[i] = 0;
+            zero1[i] = 0;
+        }
+    }
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= M) return;
     const float* row = logits + (size_t)t * E;
@@ -146,23 +154,26 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                       float* weights, const uint16_t* x, int K, uint8_t* x_q, float* x_scales,
-                      hipStream_t s) {
+                      int32_t* z0, int32_t* z1, int zn, hipStream_t s) {
     const int per = M >= kRouteWaves * device_info().cu_count ? kRouteWaves : 1;
     const int grid = (M + per - 1) / per;
     if (x_q)
         hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid), dim3(64 * per), 0, s,
-                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
+                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
+                           z1, zn);
     else
         hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * per), 0, s,
-                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales);
+                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
+                           z1, zn);
     return hipGetLastError();
 }
 
 hipError_t launch_route_any(const float* logits, int M, int E, int k, float softcap,
                             int32_t* ids, float* weights, const uint16_t* x, int K,
-                            uint8_t* x_q, float* x_scales, hipStream_t s) {
+                            uint8_t* x_q, float* x_scales, int32_t* z0, int32_t* z1, int zn,
+                            hipStream_t s) {
     if (M == 0) return hipSuccess;
-#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s
+#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0, z1, zn, s
     if (E <= 64) return launch_vpl<1>(MOE_ROUTE_ARGS);
     if (E <= 128) return launch_vpl<2>(MOE_ROUTE_ARGS);
     if (E <= 256) return launch_vpl<4>(MOE_ROUTE_ARGS);
@@ -176,13 +187,22 @@ hipError_t launch_route_any(const float* logits, int M, int E, int k, float soft
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                         float* weights, hipStream_t s) {
     return launch_route_any(logits, M, E, k, softcap, ids, weights, nullptr, 0, nullptr,
-                            nullptr, s);
+                            nullptr, nullptr, nullptr, 0, s);
 }
 
 hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
                                  int K, float softcap, int32_t* ids, float* weights,
                                  uint8_t* x_q, float* x_scales, hipStream_t s) {
-    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, s);
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales,
+                            nullptr, nullptr, 0, s);
+}
+
+hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
+                                      int k, int K, float softcap, int32_t* ids, float* weights,
+                                      uint8_t* x_q, float* x_scales, int32_t* zero0,
+                                      int32_t* zero1, int zero_n, hipStream_t s) {
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, zero0,
+                            zero1, zero_n, s);
 }
 
 }  // namespace moe

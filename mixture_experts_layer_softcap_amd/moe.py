@@ -182,8 +182,7 @@ def grouped_gemm_gather(x_q, x_scales, k: int, w_q, w_scales, tasks, ntasks, chu
 
 def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
                     flags: int = 0) -> int:
-    """Kernels moe_forward_ex launches for these arguments (3 or 4: the unstaged paths,
-    5 staged)."""
+    """Kernels moe_forward_ex launches for these arguments (3 small batch, 5 otherwise)."""
     n = lib().moe_forward_kernels(M, E, k, K, N, chunk_rows, flags)
     if n < 0:
         raise MoeError("moe_forward_kernels", n)

@@ -626,7 +626,17 @@ def test_forward_skewed_sampled(name, chunk):
     ids, _ = orc.route(d["logits"], d["k"], CAP)
     counts, _ = orc.layout(ids, d["E"])
     assert counts.min() >= 1 and counts.max() / counts.min() >= 10
-    outs = gpu_forward(d, reps=2, chunk=chunk)
+    outs, ws = gpu_forward(d, reps=2, chunk=chunk, keep_ws=True)
+    if chunk != 64:
+        # the gathering path's layout (count and sort kernels over many workgroups)
+        r_counts, r_offsets = orc.layout(ids, d["E"])
+        R = d["M"] * d["k"]
+        np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, d["E"]), r_counts)
+        np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, d["E"] + 1), r_offsets)
+        s_ids = ws_part(ws, d, 8, np.int32, R)
+        r_ids, _, _ = orc.sort_gather(ids, r_offsets, np.zeros((d["M"], 128), np.uint8),
+                                      np.zeros((d["M"], 1), np.float32))
+        np.testing.assert_array_equal(s_ids[canonical_segments(s_ids, r_offsets)], r_ids)
     # sampled tokens: first, last, a seeded spread, and tokens routed to the busiest expert
     busiest = int(np.argmax(counts))
     on_busy = np.nonzero((ids == busiest).any(1))[0]
