@@ -41,6 +41,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     return a > 0x7F800000u ? 0x7Fu : (sign | code);       // NaN
 }
 
+// Four values to OCP E4M3FN codes with the hardware converter (gfx950 V_CVT_PK_FP8_F32:
+// round to nearest even, subnormals m * 2^-9, signed zeros kept), bytes in argument order.
+// The inputs are clamped to [-448, 448] first, so |y| >= 448 gives 0x7E|sign as in
+// e4m3_encode: the same codes for every finite input (checked against it and the oracle by a
+// dense sweep of fp32 bit patterns).
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // Router selection key of logit v of expert e: the high word orders the float (-0 ranks equal
 // to +0), the low word holds 0xFFFFFFFF - e so equal logits resolve to the lower expert index.
 // Keys of one token's experts are distinct; its top-k are the k largest keys.
@@ -124,12 +138,9 @@ __device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = max16(valid ? amax : 0.0f);
     const QScale q = block_scale(amax);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(v[i] * q.inv);
     Quant8 out;
-    out.codes.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    out.codes.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    out.codes.x = e4m3_encode4(v[0] * q.inv, v[1] * q.inv, v[2] * q.inv, v[3] * q.inv);
+    out.codes.y = e4m3_encode4(v[4] * q.inv, v[5] * q.inv, v[6] * q.inv, v[7] * q.inv);
     out.scale = q.scale;
     return out;
 }

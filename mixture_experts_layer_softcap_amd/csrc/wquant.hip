@@ -40,9 +40,8 @@ __global__ __launch_bounds__(256) void wquant_kernel(const float* __restrict__ w
     const QScale q = block_scale(amax);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t c = e4m3_encode(v[i].x * q.inv) | (e4m3_encode(v[i].y * q.inv) << 8) |
-                           (e4m3_encode(v[i].z * q.inv) << 16) |
-                           (e4m3_encode(v[i].w * q.inv) << 24);
+        const uint32_t c =
+            e4m3_encode4(v[i].x * q.inv, v[i].y * q.inv, v[i].z * q.inv, v[i].w * q.inv);
         *reinterpret_cast<uint32_t*>(w_q + base + (size_t)(r0 + 8 * i) * K) = c;
     }
     if (tid == 0) w_scales[((size_t)e * Nb + nb) * Kb + kb] = q.scale;
