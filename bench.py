@@ -59,12 +59,18 @@ def measured_traffic(workload, kernel):
             rec = json.load(f)
         if rec.get("workload") != workload or not rec.get("kernel", "").startswith(kernel):
             continue
-        src = os.path.join(ROOT, rec["source"])
-        if not os.path.exists(src):
-            continue
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() == rec["source_sha256"]:
-                return rec["traffic_bytes"]
+        # every source file the kernel is built from must be unchanged since the counters
+        srcs = rec.get("sources") or {rec["source"]: rec["source_sha256"]}
+        same = True
+        for rel, sha in srcs.items():
+            path = os.path.join(ROOT, rel)
+            if not os.path.exists(path):
+                same = False
+                break
+            with open(path, "rb") as f:
+                same &= hashlib.sha256(f.read()).hexdigest() == sha
+        if same:
+            return rec["traffic_bytes"]
     return None
 
 
@@ -173,7 +179,8 @@ def bench_bf16_gemm(args, moe, synth, torch, np):
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (STORE_BF16)",
                      "achieved": round(tflops, 2), "peak": BF16_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": gbytes,
+                     "traffic": measured_traffic(args.workload, "gemm_bf16_kernel"),
+                     "algorithmic_bytes_per_launch": gbytes,
                      "hbm_frac": round(gbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(us, 3)},
     }
