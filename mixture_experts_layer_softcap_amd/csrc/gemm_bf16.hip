@@ -12,13 +12,18 @@
 //
 // Operands.  Both tiles go from global memory straight into LDS with global_load_lds_dwordx4:
 // one instruction moves 8 whole 128-byte row segments (64 k values of 8 rows), each 16-byte
-// chunk c of row r stored at position c ^ (r % 8), so the DMA reads whole cache lines and the
-// MFMA fragment reads (32 rows x one 16-byte chunk) are free of LDS bank conflicts.  Two
-// stages of 64 KiB alternate; one barrier per k step publishes a stage and frees the other.
-// The operand reads are written as inline ds_read_b128 with explicit lgkmcnt waits tied to
-// the fragment registers: the compiler cannot tell a DMA into one stage from reads of the
-// other and would otherwise drain the DMA before every read.  Rows past rc repeat row rb
-// (never stored).
+// chunk c of row r stored at position c ^ ((r/2) % 8), so the DMA reads whole cache lines and
+// the MFMA fragment reads are free of LDS bank conflicts.  Two stages of 64 KiB alternate;
+// one barrier per k step publishes a stage and frees the other.  The next stage's DMA
+// instructions are spread over the current stage's MFMAs, and each 16-wide step's fragments
+// are read during the previous step's MFMAs.  The operand reads are inline ds_read_b128 with
+// explicit lgkmcnt waits tied to the fragment registers: the compiler cannot tell a DMA into
+// one stage from reads of the other and would otherwise drain the DMA before every read.
+// Rows past rc repeat row rb + rc - 1 (never stored).
+//
+// Order.  Workgroups go round-robin over the 8 XCDs; each XCD takes one contiguous run of the
+// chunk-major task list, regrouped so that the tiles it runs together cover a few chunks x a
+// few panels (fewer distinct operand slices per k step in its L2).
 //
 // Epilogues.  STORE_F32 / STORE_BF16 write h; SWIGLU_BF16 computes a 128-column block of
 // act = bf16(silu(g) * u) from the gate columns [nb*128, nb*128+128) and the up columns
@@ -56,12 +61,17 @@ __device__ __forceinline__ i32x4 lds_read16(uint32_t addr) {
     return v;
 }
 
-// every LDS read issued so far has landed in the eight fragment registers
+// The LDS reads issued before the last N (of this wave) have landed in the eight fragment
+// registers.  The registers are in-out operands of the wait, so the compiler cannot use or
+// move their values before it; reads stay in one asm statement each and nothing else touches
+// a fragment register between its read and its wait.
+template <int N>
 __device__ __forceinline__ void lds_wait(i32x4& a0, i32x4& a1, i32x4& a2, i32x4& a3,
                                          i32x4& b0, i32x4& b1, i32x4& b2, i32x4& b3) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
+    asm volatile("s_waitcnt lgkmcnt(%8)"
                  : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1), "+v"(b2),
-                   "+v"(b3));
+                   "+v"(b3)
+                 : "i"(N));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -70,7 +80,7 @@ template <int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
                       const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
-                      void* __restrict__ out, int K, int N) {
+                      void* __restrict__ out, int K, int N, int pw, int gch) {
     __shared__ uint4 sA[2][kBM * 8];             // 2 stages x 256 rows x 128 bytes
     __shared__ uint4 sW[2][kBN * 8];
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so workgroup b
@@ -79,8 +89,19 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     // walk K in near lockstep, out of that XCD's L2.
     const int nt = *ntasks;
     const int per_xcd = (nt + 7) >> 3;
-    const int task = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if ((int)(blockIdx.x >> 3) >= per_xcd || task >= nt) return;
+    const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || t >= nt) return;
+    // Inside a run, gch consecutive chunks (same expert where possible) are taken pw panels
+    // at a time: the ~32 tiles an XCD runs together then cover gch chunks x pw panels, so
+    // each k step asks its L2 for gch + pw distinct slices instead of ~3 + N/256.
+    const int nbk = N / kBN;                    // tasks per chunk (both epilogue layouts)
+    const int grp = t / (gch * nbk);
+    const int gc = min(gch, nt / nbk - grp * gch);
+    int i = t - grp * gch * nbk;
+    const int pb = i / (gc * pw);
+    const int pwb = min(pw, nbk - pb * pw);
+    i -= pb * gc * pw;
+    const int task = (grp * gch + i / pwb) * nbk + pb * pw + i % pwb;
     const int4 td = tasks[task];
     const int e = td.x, rb = td.y, rc = td.z, nb = td.w;
     const int lane = threadIdx.x & 63;
@@ -149,38 +170,80 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     }
     constexpr uint32_t kStage = 256 * 128;      // bytes per stage buffer
 
-    auto compute = [&](uint32_t boff) {
+    // One k step from buffer boff.  With DMA, the next step's 16 DMA instructions are spread
+    // over the step's 64 MFMAs (one after every fourth): a wave issues in order, and a burst
+    // of DMA instructions stalls it on the memory pipeline long enough to hold back its
+    // MFMAs, so the two would otherwise run one after the other.
+    // Fragments of one 16-wide k step: 4 of A, 4 of W
+    struct Frag {
+        i32x4 a0, a1, a2, a3, w0, w1, w2, w3;
+    };
+    auto read_frags = [&](Frag& f, uint32_t boff, int st) __attribute__((always_inline)) {
+        const uint32_t qa = pa[st] + boff, qw0 = pw0[st] + boff, qw2 = pw2[st] + boff;
+        f.a0 = lds_read16<0 * 4096>(qa);
+        f.a1 = lds_read16<1 * 4096>(qa);
+        f.a2 = lds_read16<2 * 4096>(qa);
+        f.a3 = lds_read16<3 * 4096>(qa);
+        f.w0 = lds_read16<0>(qw0);
+        f.w1 = lds_read16<4096>(qw0);
+        f.w2 = lds_read16<0>(qw2);
+        f.w3 = lds_read16<4096>(qw2);
+    };
+
+    // One k step from buffer boff: the fragments of 16-wide step st+1 are read while the
+    // MFMAs of step st run.  With DMA, the next k step's 16 DMA instructions are spread over
+    // the step's 64 MFMAs (one after every fourth): a wave issues in order, and a burst of DMA
+    // instructions stalls it on the memory pipeline long enough to hold back its MFMAs, so
+    // the two would otherwise run one after the other.
+    auto compute = [&](uint32_t boff, int nbuf, int nkt, auto with_dma) {
+        uint4* dA = sA[nbuf];
+        uint4* dW = sW[nbuf];
+        const int k0 = nkt * kBK;
+        Frag f[2];
+        read_frags(f[0], boff, 0);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const uint32_t qa = pa[st] + boff, qw0 = pw0[st] + boff, qw2 = pw2[st] + boff;
-            i32x4 fa0 = lds_read16<0 * 4096>(qa);
-            i32x4 fa1 = lds_read16<1 * 4096>(qa);
-            i32x4 fa2 = lds_read16<2 * 4096>(qa);
-            i32x4 fa3 = lds_read16<3 * 4096>(qa);
-            i32x4 fw0 = lds_read16<0>(qw0);
-            i32x4 fw1 = lds_read16<4096>(qw0);
-            i32x4 fw2 = lds_read16<0>(qw2);
-            i32x4 fw3 = lds_read16<4096>(qw2);
-            lds_wait(fa0, fa1, fa2, fa3, fw0, fw1, fw2, fw3);
-            const bf16x8 A[4] = {as_bf16x8(fa0), as_bf16x8(fa1), as_bf16x8(fa2), as_bf16x8(fa3)};
-            const bf16x8 B[4] = {as_bf16x8(fw0), as_bf16x8(fw1), as_bf16x8(fw2), as_bf16x8(fw3)};
+            Frag& c = f[st & 1];
+            if (st < 3) {
+                read_frags(f[(st + 1) & 1], boff, st + 1);
+                lds_wait<8>(c.a0, c.a1, c.a2, c.a3, c.w0, c.w1, c.w2, c.w3);
+            } else {
+                lds_wait<0>(c.a0, c.a1, c.a2, c.a3, c.w0, c.w1, c.w2, c.w3);
+            }
+            const bf16x8 A[4] = {as_bf16x8(c.a0), as_bf16x8(c.a1), as_bf16x8(c.a2),
+                                 as_bf16x8(c.a3)};
+            const bf16x8 B[4] = {as_bf16x8(c.w0), as_bf16x8(c.w1), as_bf16x8(c.w2),
+                                 as_bf16x8(c.w3)};
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[ni], A[mi],
                                                                          acc[mi][ni], 0, 0, 0);
+                if constexpr (decltype(with_dma)::value) {
+                    const int i = 2 * st + (mi >> 1);          // DMA row group of this wave
+                    const int row0 = wave * 64 + i * 8;
+                    if (mi & 1)
+                        __builtin_amdgcn_global_load_lds(srcW[i] + k0,
+                                                         (lds_void*)(dW + row0 * 8), 16, 0, 0);
+                    else
+                        __builtin_amdgcn_global_load_lds(srcA[i] + k0,
+                                                         (lds_void*)(dA + row0 * 8), 16, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
     // k step kt on buffer kt%2: wait for it (the DMA of step kt+1 is not issued yet), publish
-    // it and free the other buffer, start step kt+1 there, compute
+    // it and free the other buffer, compute while the DMA of step kt+1 fills that buffer
     issue(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
         barrier_after_vmcnt<0>();
-        if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
-        compute((kt & 1) ? kStage : 0u);
+        compute((kt & 1) ? kStage : 0u, (kt + 1) & 1, kt + 1, std::integral_constant<bool, true>{});
     }
+    barrier_after_vmcnt<0>();
+    compute(((nk - 1) & 1) ? kStage : 0u, 0, 0, std::integral_constant<bool, false>{});
 
     // C layout of the 32x32 MFMA: lane (j, h) holds column j (routed row) and, in register
     // r, output row 8*(r/4) + 4*h + r%4 of the 32-row weight group
@@ -242,18 +305,21 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
     if (max_tasks <= 0) return hipSuccess;
     const int4* t = reinterpret_cast<const int4*>(tasks);
     const int grid = (max_tasks + 7) / 8 * 8;    // whole rounds of the 8 XCDs
+    // tile groups of ~32 (one XCD's CUs): up to 8 panels x 32/8 chunks
+    const int pw = min(8, N / kBN);
+    const int gch = 32 / pw;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_BF16>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
             break;
         case MOE_EPI_SWIGLU_BF16:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_SWIGLU_BF16>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
             break;
         default:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_F32>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
     }
     return hipGetLastError();
 }
