@@ -78,7 +78,7 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
                           const uint8_t* __restrict__ w, const float* __restrict__ w_scales,
                           const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                           const int32_t* __restrict__ sorted_route_ids, void* __restrict__ out,
-                          int rows, int K, int N, int pairs, int chunks_per_xcd, int kr) {
+                          int rows, int K, int N, int pairs, int cus_x, int kr) {
     using Cfg = TileCfg<BM>;
     constexpr int S = Cfg::kStages;
     __shared__ TileStage<BM> st0, st1, st2;     // st2 is used only with three stages
@@ -96,14 +96,31 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
     const int Nb = N >> 7;
     const int xcd = (int)(blockIdx.x & 7);
     const int slot = (int)(blockIdx.x >> 3);
-    const int qc = slot / pairs;
-    const int hp = slot - qc * pairs;
-    if (qc >= chunks_per_xcd) return;
-    const int task = (qc * 8 + xcd) * Nb + 2 * hp;
-    if (task >= *ntasks) return;
+    // The XCD runs its P panel-pair items on cus_x CUs; when its last round would hold r <=
+    // cus_x/2 items, those r items run as 2r single panels instead (a round of pairs then ends
+    // in a shorter round of singles).
+    const int nt = *ntasks;
+    const int ncx = ((nt + Nb - 1) / Nb - xcd + 7) >> 3;  // chunks xcd, xcd + 8, ...
+    const int P = ncx * pairs;
+    const int r = P % cus_x;
+    const int R = 2 * r <= cus_x ? r : 0;
+    int q, nb0, np;
+    if (slot < P - R) {
+        q = slot;
+        nb0 = 2 * (q % pairs);
+        np = min(2, Nb - nb0);
+    } else {
+        const int i = slot - (P - R);
+        if (i >= 2 * R) return;
+        q = P - R + (i >> 1);
+        nb0 = 2 * (q % pairs) + (i & 1);
+        np = 1;
+        if (nb0 >= Nb) return;                    // odd Nb: the last pair has one panel
+    }
+    const int task = (xcd + 8 * (q / pairs)) * Nb + nb0;
+    if (task >= nt) return;
     const int4 td = tasks[task];
-    const int e = td.x, rb = td.y, rc = td.z, nb0 = td.w;   // nb0 = 2 * hp
-    const int np = min(2, Nb - nb0);              // panels in this slab (1 or 2)
+    const int e = td.x, rb = td.y, rc = td.z;     // td.w == nb0
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,16 +296,17 @@ hipError_t launch_epi(const uint8_t* a, const float* a_scales, int rows, int K,
     const int pairs = (Nb + 1) / 2;
     const int max_chunks = (max_tasks + Nb - 1) / Nb;
     const int cpx = (max_chunks + 7) / 8;
-    const unsigned grid = (unsigned)(8 * cpx * pairs);
+    const int cus_x = max(2, device_info().cu_count / 8);   // CUs per XCD
+    const unsigned grid = (unsigned)(8 * (cpx * pairs + cus_x / 2));
     const int4* t = reinterpret_cast<const int4*>(tasks);
     if (K == 2048)
         hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 16, GATHER>), dim3(grid),
                            dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted, out,
-                           rows, K, N, pairs, cpx, kr);
+                           rows, K, N, pairs, cus_x, kr);
     else
         hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, 0, GATHER>), dim3(grid),
                            dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted, out,
-                           rows, K, N, pairs, cpx, kr);
+                           rows, K, N, pairs, cus_x, kr);
     return hipGetLastError();
 }
 
