@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
             "orc_forward_tokens": (I, [P, P, P, P, I, I, I, I, I, F, P, I, P, P]),
             "orc_gemm_bf16": (I, [P, I, I, P, I, P, I, P, I, P, P]),
             "orc_ffn_tokens": (I, [P, P, P, P, I, I, I, I, I, F, P, I, P, P]),
+            "orc_swiglu_f32": (I, [P, I, I, P]),
+            "orc_quant_rows_f32": (I, [P, I, I, P, P]),
+            "orc_mlp_tokens": (I, [P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -283,4 +286,43 @@ def ffn_tokens(logits, x_bf16, w_up, w_down, k: int, cap: float, tokens=None):
     _check(lib().orc_ffn_tokens(_p(logits), _p(x), _p(w_up), _p(w_down), M, E, k, H, F, cap,
                                 _p(tl), 0 if tl is None else n, _p(y), _p(y64)),
            "orc_ffn_tokens")
+    return y, y64
+
+
+def swiglu_f32(h: np.ndarray) -> np.ndarray:
+    """act = fp32(silu(g) * u) for h [rows][2I] (gate columns first)."""
+    h = _c(h, np.float64)
+    rows, I2 = h.shape
+    act = np.zeros((rows, I2 // 2), np.float32)
+    _check(lib().orc_swiglu_f32(_p(h), rows, I2 // 2, _p(act)), "orc_swiglu_f32")
+    return act
+
+
+def quant_rows_f32(v: np.ndarray):
+    v = _c(v, np.float32)
+    rows, K = v.shape
+    q = np.zeros((rows, K), np.uint8)
+    s = np.zeros((rows, K // 128), np.float32)
+    _check(lib().orc_quant_rows_f32(_p(v), rows, K, _p(q), _p(s)), "orc_quant_rows_f32")
+    return q, s
+
+
+def mlp_tokens(logits, x_bf16, w1_q, w1_scales, w2_q, w2_scales, k: int, cap: float,
+               tokens=None):
+    logits = _c(logits, np.float32)
+    x = _c(x_bf16, np.uint16)
+    w1_q = _c(w1_q, np.uint8)
+    w1_scales = _c(w1_scales, np.float32)
+    w2_q = _c(w2_q, np.uint8)
+    w2_scales = _c(w2_scales, np.float32)
+    M, E = logits.shape
+    H = x.shape[1]
+    I = w2_q.shape[2]
+    tl = None if tokens is None else _c(tokens, np.int32)
+    n = M if tl is None else tl.shape[0]
+    y = np.zeros((n, H), np.uint16)
+    y64 = np.zeros((n, H), np.float64)
+    _check(lib().orc_mlp_tokens(_p(logits), _p(x), _p(w1_q), _p(w1_scales), _p(w2_q),
+                                _p(w2_scales), M, E, k, H, I, cap, _p(tl),
+                                0 if tl is None else n, _p(y), _p(y64)), "orc_mlp_tokens")
     return y, y64

@@ -487,3 +487,91 @@ done:
     free(ids); free(wts); free(h); free(act); free(acc);
     return rc;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* [FMF8] comparison section, "vLLM full MLP" reference: gate+up, SiLU, down in FP8     */
+/* ------------------------------------------------------------------------------------ */
+
+int orc_swiglu_f32(const double* h, int rows, int I, float* act) {
+    if (!h || !act || rows < 0 || I < 1) return -1;
+    for (long r = 0; r < rows; ++r)
+        for (int f = 0; f < I; ++f) {
+            double g = h[r * 2 * I + f], u = h[r * 2 * I + I + f];
+            act[r * I + f] = (float)(g / (1.0 + exp(-g)) * u);
+        }
+    return 0;
+}
+
+int orc_quant_rows_f32(const float* v, int rows, int K, uint8_t* q, float* scales) {
+    if (!v || !q || !scales || rows < 0 || K < QBLK || K % QBLK) return -1;
+    int Kb = K / QBLK;
+    for (long r = 0; r < rows; ++r)
+        for (int b = 0; b < Kb; ++b)
+            quant_block(v + r * K + b * QBLK, QBLK, q + r * K + b * QBLK, &scales[r * Kb + b]);
+    return 0;
+}
+
+/* one row of the block-scaled FP8 GEMM: out[n] = sum_b sa[b] * sw[e][n/128][b] *
+ * sum_{i in block b} e4m3(a[i]) * e4m3(w[e][n][i]) */
+static void gemm_fp8_row(const double* dq, const uint8_t* a, const float* sa,
+                         const uint8_t* w, const float* sw, int e, int N, int K, double* out) {
+    int Nb = N / QBLK, Kb = K / QBLK;
+    for (int n = 0; n < N; ++n) {
+        const uint8_t* wr = w + ((size_t)e * N + n) * K;
+        double c = 0.0;
+        for (int b = 0; b < Kb; ++b) {
+            double bs = 0.0;
+            for (int i = b * QBLK; i < (b + 1) * QBLK; ++i) bs += dq[a[i]] * dq[wr[i]];
+            c += bs * (double)sa[b] * (double)sw[((size_t)e * Nb + n / QBLK) * Kb + b];
+        }
+        out[n] = c;
+    }
+}
+
+int orc_mlp_tokens(const float* logits, const uint16_t* x, const uint8_t* w1_q,
+                   const float* w1_scales, const uint8_t* w2_q, const float* w2_scales,
+                   int M, int E, int k, int H, int I, float cap, const int32_t* tokens,
+                   int ntok, uint16_t* y, double* y64) {
+    if (!logits || !x || !w1_q || !w1_scales || !w2_q || !w2_scales || !y || M < 1 || E < 1 ||
+        k < 1 || k > E || H < QBLK || H % QBLK || I < QBLK || I % QBLK || ntok < 0)
+        return -1;
+    int n_out = tokens ? ntok : M;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * k);
+    float* wts = (float*)malloc(sizeof(float) * k);
+    uint8_t* xq = (uint8_t*)malloc((size_t)H);
+    float* xs = (float*)malloc(sizeof(float) * (H / QBLK));
+    double* h1 = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+    float* act = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* aq = (uint8_t*)malloc((size_t)I);
+    float* as = (float*)malloc(sizeof(float) * (I / QBLK));
+    double* h2 = (double*)malloc(sizeof(double) * (size_t)H);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+    double dq[256];
+    int rc = -1;
+    if (!ids || !wts || !xq || !xs || !h1 || !act || !aq || !as || !h2 || !acc) goto done;
+    for (int c = 0; c < 256; ++c) dq[c] = orc_e4m3_value((uint8_t)c);
+    for (int i = 0; i < n_out; ++i) {
+        int t = tokens ? tokens[i] : i;
+        if (t < 0 || t >= M) goto done;
+        if (orc_route(logits + (size_t)t * E, 1, E, k, cap, ids, wts)) goto done;
+        if (orc_quant_act(x + (size_t)t * H, 1, H, xq, xs)) goto done;
+        for (int n = 0; n < H; ++n) acc[n] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = ids[j];
+            gemm_fp8_row(dq, xq, xs, w1_q, w1_scales, e, 2 * I, H, h1);
+            if (orc_swiglu_f32(h1, 1, I, act)) goto done;
+            if (orc_quant_rows_f32(act, 1, I, aq, as)) goto done;
+            gemm_fp8_row(dq, aq, as, w2_q, w2_scales, e, H, I, h2);
+            for (int n = 0; n < H; ++n) acc[n] += (double)wts[j] * h2[n];
+        }
+        for (int n = 0; n < H; ++n) {
+            y[(size_t)i * H + n] = orc_bf16_from_double(acc[n]);
+            if (y64) y64[(size_t)i * H + n] = acc[n];
+        }
+    }
+    rc = 0;
+done:
+    free(ids); free(wts); free(xq); free(xs); free(h1); free(act); free(aq); free(as);
+    free(h2); free(acc);
+    return rc;
+}

@@ -117,6 +117,26 @@ int orc_ffn_tokens(const float* logits, const uint16_t* x, const uint16_t* w_up,
                    const uint16_t* w_down, int M, int E, int k, int H, int F, float cap,
                    const int32_t* tokens, int ntok, uint16_t* y, double* y64);
 
+/* ---- [FMF8] comparison section, "vLLM full MLP" reference: the expert MLP around the
+ * grouped GEMM (gate+up projection, SiLU gating, down projection), here in FP8 ---------- */
+/* act[r][f] = fp32(silu(g) * u) with g = h[r][f], u = h[r][I + f] and
+ * silu(g) = g / (1 + e^-g), formed in double and rounded once to fp32. */
+int orc_swiglu_f32(const double* h, int rows, int I, float* act);
+/* The QSG quantiser on fp32 rows: per row and 128-column block, scale = fp32(amax/448),
+ * code = e4m3(fp32(v * fp32(1/scale))); codes [rows][K], scales [rows][K/128]. */
+int orc_quant_rows_f32(const float* v, int rows, int K, uint8_t* q, float* scales);
+/* The layer for the listed tokens (all when tokens is NULL), in stage order: route; x
+ * quantised per 128 (orc_quant_act); per route j of token t with expert e,
+ *   h1 = the block-scaled FP8 GEMM of x_q against w1[e] [2I][H] (rows 0..I-1 gate, I..2I-1
+ *        up; scales w1_scales [E][2I/128][H/128]),
+ *   act = orc_swiglu_f32(h1), requantised per 128 (orc_quant_rows_f32),
+ *   h2 = the block-scaled FP8 GEMM of act_q against w2[e] [H][I] (scales [E][H/128][I/128]);
+ * y[t] = bf16(sum_j w_j h2_j), all sums in double. */
+int orc_mlp_tokens(const float* logits, const uint16_t* x, const uint8_t* w1_q,
+                   const float* w1_scales, const uint8_t* w2_q, const float* w2_scales,
+                   int M, int E, int k, int H, int I, float cap, const int32_t* tokens,
+                   int ntok, uint16_t* y, double* y64);
+
 #ifdef __cplusplus
 }
 #endif
