@@ -293,6 +293,39 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
                     uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                     moe_stream_t stream);
 
+/* ---- [FMF8] comparison section, "vLLM full MLP" reference, in FP8 ----------------------
+ * The activation step of the expert MLP: for each of `rows` rows of h f32 [rows][2I] (gate
+ * columns 0..I-1, up columns I..2I-1; device memory), act = silu(g) * u in fp32 with
+ * silu(g) = g / (1 + e^-g), then the QSG quantiser per 128 columns (scale = amax/448, code =
+ * e4m3(act * (1/scale)), an all-zero block gets scale 0) into a_q E4M3 [rows][I] and
+ * a_scales f32 [I/128][rows] (transposed, as moe_quant_sort_gather writes them).  I a
+ * positive multiple of 128.  One launch on `stream`. */
+int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_scales,
+                     moe_stream_t stream);
+
+/* The whole expert MLP layer in FP8:
+ *   route (softcap, top-k) -> layouts of both GEMMs -> x quantised, sorted and gathered
+ *   (moe_quant_sort_gather) -> gate+up grouped FP8 GEMM (fp32 rows, sorted order) ->
+ *   moe_swiglu_quant -> down grouped FP8 GEMM (fp32 rows at route ids) -> routing-weighted
+ *   combine:
+ *   h1 = x_q[t] (*) w1[e]  (block-scaled, [2I] per route),  act_q = quant(silu(g) * u),
+ *   y[t] = bf16( sum_j w_tj * act_q[r_j] (*) w2[e_j] )
+ * logits f32 [M][E], x bf16 [M][H], w1_q E4M3 [E][2I][H] with w1_scales f32
+ * [E][2I/128][H/128] (gate rows then up rows), w2_q E4M3 [E][H][I] with w2_scales f32
+ * [E][H/128][I/128] -> out bf16 [M][H].  H and I positive multiples of 128; chunk_rows as in
+ * moe_forward_ex (0 picks it from the batch).  Workspace of moe_mlp_workspace_bytes(...)
+ * bytes; parts (for inspection): 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors,
+ * 5 gate+up tasks, 6 down tasks, 7 ntasks (gate+up, down) at +0 and queue pairs at +16,
+ * 8 sorted_route_ids, 9 route_slots, 10 x codes (sorted), 11 x scales, 12 gate+up rows f32
+ * [M*k][2I], 13 act codes [M*k][I], 14 act scales [I/128][M*k], 15 down rows f32 [M*k][H]
+ * at route ids.  Eight plain launches on `stream`, no host synchronisation. */
+size_t moe_mlp_workspace_bytes(int M, int E, int k, int H, int I);
+int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which);
+int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
+                    const float* w1_scales, const uint8_t* w2_q, const float* w2_scales, int M,
+                    int E, int k, int H, int I, float softcap, uint16_t* out, void* workspace,
+                    size_t workspace_bytes, int chunk_rows, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -288,6 +288,48 @@ FfnLayout ffn_layout(int M, int E, int k, int H, int F) {
     L.total = p;
     return L;
 }
+
+// ---- FP8 expert MLP layer ---------------------------------------------------------------
+constexpr int kMlpParts = 16;
+struct MlpLayout {
+    size_t off[kMlpParts];
+    size_t total;
+};
+bool mlp_dims_ok(int M, int E, int k, int H, int I) {
+    return M >= 1 && route_dims_ok(M, E, k) && H >= 128 && H % 128 == 0 && I >= 128 &&
+           I % 128 == 0 && (long long)M * k * (long long)(H > 2 * I ? H : 2 * I) < (1LL << 40);
+}
+MlpLayout mlp_layout(int M, int E, int k, int H, int I) {
+    const size_t R = (size_t)M * k;
+    const size_t tu = (size_t)max_tasks_ll(M, k, E, 2 * I / 128, 1);  // any chunk_rows fits
+    const size_t td = (size_t)max_tasks_ll(M, k, E, H / 128, 1);
+    const size_t sz[kMlpParts] = {
+        R * 4,                        // 0 topk_ids
+        R * 4,                        // 1 topk_weights
+        (size_t)E * 4,                // 2 counts
+        (size_t)(E + 1) * 4,          // 3 offsets
+        (size_t)E * 4,                // 4 cursors
+        tu * sizeof(moe_task),        // 5 gate+up tasks
+        td * sizeof(moe_task),        // 6 down tasks
+        32,                           // 7 ntasks (2) at +0, queue pairs (2 x 2) at +16
+        R * 4,                        // 8 sorted_route_ids
+        R * 4,                        // 9 route_slots
+        R * (size_t)H,                // 10 x codes, sorted
+        (size_t)(H / 128) * R * 4,    // 11 x scales [H/128][R]
+        R * (size_t)(2 * I) * 4,      // 12 gate+up rows f32, sorted
+        R * (size_t)I,                // 13 act codes, sorted
+        (size_t)(I / 128) * R * 4,    // 14 act scales [I/128][R]
+        R * (size_t)H * 4,            // 15 down rows f32 at route ids
+    };
+    MlpLayout L;
+    size_t p = 0;
+    for (int i = 0; i < kMlpParts; ++i) {
+        L.off[i] = p;
+        p = align256(p + sz[i]);
+    }
+    L.total = p;
+    return L;
+}
 }  // namespace moe
 
 using namespace moe;
@@ -590,6 +632,85 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
         (e = launch_gemm_bf16(act, F, w_down, H, td, nt + 1, mtd, MOE_EPI_STORE_F32, down, s)) !=
             hipSuccess ||
         (e = launch_scatter(down, slots, wts, ids, M, k, E, H, out, s)) != hipSuccess)
+        return hip_status(e);
+    return MOE_OK;
+}
+
+// ---- FP8 expert MLP layer ---------------------------------------------------------------
+int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_scales,
+                     moe_stream_t stream) {
+    if (rows < 0 || I < 128 || I % 128 || (long long)rows * 2 * I >= (1LL << 40))
+        return MOE_E_INVAL;
+    if (rows > 0 && (!h || !a_q || !a_scales)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_swiglu_quant(h, rows, I, a_q, a_scales, (hipStream_t)stream));
+}
+
+size_t moe_mlp_workspace_bytes(int M, int E, int k, int H, int I) {
+    if (!mlp_dims_ok(M, E, k, H, I)) return 0;
+    return mlp_layout(M, E, k, H, I).total;
+}
+
+int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which) {
+    if (!mlp_dims_ok(M, E, k, H, I) || which < 0 || which >= kMlpParts) return -1;
+    return (int64_t)mlp_layout(M, E, k, H, I).off[which];
+}
+
+int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
+                    const float* w1_scales, const uint8_t* w2_q, const float* w2_scales, int M,
+                    int E, int k, int H, int I, float softcap, uint16_t* out, void* workspace,
+                    size_t workspace_bytes, int chunk_rows, moe_stream_t stream) {
+    if (!mlp_dims_ok(M, E, k, H, I)) return MOE_E_INVAL;
+    if (!logits || !x || !w1_q || !w1_scales || !w2_q || !w2_scales || !out || !workspace)
+        return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    const int Kmax = H > I ? H : I;
+    if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && Kmax > 8192))
+        return MOE_E_INVAL;
+    const MlpLayout L = mlp_layout(M, E, k, H, I);
+    if (workspace_bytes < L.total) return MOE_E_NOSPC;
+    int rc = check_device();
+    if (rc) return rc;
+    int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, H);
+    if (!chunk_rows && chunk > 64 && Kmax > 8192) chunk = 64;
+    char* base = static_cast<char*>(workspace);
+    auto at = [&](int i) { return base + L.off[i]; };
+    int32_t* ids = reinterpret_cast<int32_t*>(at(0));
+    float* wts = reinterpret_cast<float*>(at(1));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(2));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(3));
+    int32_t* cursors = reinterpret_cast<int32_t*>(at(4));
+    moe_task* tu = reinterpret_cast<moe_task*>(at(5));
+    moe_task* td = reinterpret_cast<moe_task*>(at(6));
+    int32_t* nt = reinterpret_cast<int32_t*>(at(7));
+    uint32_t* queue = reinterpret_cast<uint32_t*>(at(7) + 16);
+    int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
+    int32_t* slots = reinterpret_cast<int32_t*>(at(9));
+    uint8_t* xq = reinterpret_cast<uint8_t*>(at(10));
+    float* xs = reinterpret_cast<float*>(at(11));
+    float* h1 = reinterpret_cast<float*>(at(12));
+    uint8_t* aq = reinterpret_cast<uint8_t*>(at(13));
+    float* as = reinterpret_cast<float*>(at(14));
+    float* h2 = reinterpret_cast<float*>(at(15));
+    const int R = M * k;
+    const int nbu = 2 * I / 128, nbd = H / 128;
+    const int mtu = (int)max_tasks_ll(M, k, E, nbu, chunk);
+    const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
+        (e = launch_layout(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu, mtu, nt,
+                           queue, nullptr, nullptr, s)) != hipSuccess ||
+        (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
+                           nt + 1, queue + 2, nullptr, nullptr, s)) != hipSuccess ||
+        (e = launch_qsg(x, M, H, ids, k, E, cursors, sorted, slots, xq, xs, s)) != hipSuccess ||
+        (e = launch_gemm_fp8(xq, xs, R, H, w1_q, w1_scales, E, 2 * I, tu, nt, mtu, chunk, queue,
+                             MOE_EPI_STORE_F32, sorted, h1, s)) != hipSuccess ||
+        (e = launch_swiglu_quant(h1, R, I, aq, as, s)) != hipSuccess ||
+        (e = launch_gemm_fp8(aq, as, R, I, w2_q, w2_scales, E, H, td, nt + 1, mtd, chunk,
+                             queue + 2, MOE_EPI_ROUTE_F32, sorted, h2, s)) != hipSuccess ||
+        (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s)) != hipSuccess)
         return hip_status(e);
     return MOE_OK;
 }

@@ -125,14 +125,8 @@ struct Quant8 {
     float scale;
 };
 
-__device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
-    float v[8];
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
+// The same on 8 fp32 values (the requantiser of the expert MLP's activations).
+__device__ __forceinline__ Quant8 quantise8_f32(const float (&v)[8], bool valid) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -143,6 +137,17 @@ __device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
     out.codes.y = e4m3_encode4(v[4] * q.inv, v[5] * q.inv, v[6] * q.inv, v[7] * q.inv);
     out.scale = q.scale;
     return out;
+}
+
+__device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    return quantise8_f32(v, valid);
 }
 
 // ---- matrix-core operands and vector-memory ordering ----

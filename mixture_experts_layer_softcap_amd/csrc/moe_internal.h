@@ -99,6 +99,10 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                             int epilogue, void* out, hipStream_t s);
 
+// silu(g) * u requantised per 128 columns (the FP8 expert MLP's activation step)
+hipError_t launch_swiglu_quant(const float* h, int R, int I, uint8_t* a_q, float* a_scales,
+                               hipStream_t s);
+
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
                           hipStream_t s);

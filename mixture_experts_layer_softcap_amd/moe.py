@@ -58,6 +58,11 @@ SIGNATURES = {
     "moe_ffn_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_ffn_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _P]),
+    "moe_swiglu_quant": (_I, [_P, _I, _I, _P, _P, _P]),
+    "moe_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "moe_mlp_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
+    "moe_mlp_forward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I,
+                             _P]),
 }
 
 _lib = None
@@ -254,3 +259,31 @@ def ffn_forward(logits, x, w_up, w_down, k: int, softcap: float, out, workspace,
     _call("moe_ffn_forward", _ptr(logits), _ptr(x), _ptr(w_up), _ptr(w_down), M, E, k, H, F,
           softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
           chunk_rows, _stream(stream))
+
+
+def swiglu_quant(h, a_q, a_scales, stream=None):
+    """h f32 [rows][2I] -> a_q uint8 [rows][I], a_scales f32 [I/128][rows]."""
+    rows, I2 = h.shape
+    _call("moe_swiglu_quant", _ptr(h), rows, I2 // 2, _ptr(a_q), _ptr(a_scales),
+          _stream(stream))
+
+
+def mlp_workspace_bytes(M: int, E: int, k: int, H: int, I: int) -> int:
+    v = lib().moe_mlp_workspace_bytes(M, E, k, H, I)
+    if v == 0:
+        raise MoeError("moe_mlp_workspace_bytes", MOE_E_INVAL)
+    return v
+
+
+def mlp_workspace_offset(M: int, E: int, k: int, H: int, I: int, which: int) -> int:
+    return lib().moe_mlp_workspace_offset(M, E, k, H, I, which)
+
+
+def mlp_forward(logits, x, w1_q, w1_scales, w2_q, w2_scales, k: int, softcap: float, out,
+                workspace, chunk_rows: int = 0, stream=None):
+    M, E = logits.shape
+    H = x.shape[1]
+    I = w2_q.shape[2]
+    _call("moe_mlp_forward", _ptr(logits), _ptr(x), _ptr(w1_q), _ptr(w1_scales), _ptr(w2_q),
+          _ptr(w2_scales), M, E, k, H, I, softcap, _ptr(out), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream))

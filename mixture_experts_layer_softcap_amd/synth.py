@@ -93,6 +93,57 @@ def workload_inputs(name: str, seed: int = 0, weights: bool = True):
     return d
 
 
+# ---- FP8 expert MLP inputs ---------------------------------------------------------------
+
+# exponent fields 8..15 of the E4M3 weight codes, weighted like |N(0, 1)| * 112 (4 sigma near
+# the largest finite value 448): counts out of 256 per field
+_E4M3_EXP_COUNTS = [(8, 5), (9, 10), (10, 20), (11, 41), (12, 64), (13, 64), (14, 39), (15, 13)]
+_E4M3_EXP_EDGES = np.cumsum([c for _, c in _E4M3_EXP_COUNTS])[:-1]   # 7 thresholds in 0..255
+
+
+def fp8_weight_codes(shape, g: np.random.Generator) -> np.ndarray:
+    """Seeded E4M3 codes from one random 16-bit draw each: bits 0-7 pick the exponent field
+    8 + #(edges <= byte), bits 8-10 the mantissa, bit 11 the sign (the NaN pattern 0x7F is
+    moved to 0x7E).  Drawn one leading-axis slice at a time (small temporaries)."""
+    out = np.empty(shape, np.uint8)
+    for i in range(shape[0]):
+        r = g.integers(0, 1 << 16, size=shape[1:], dtype=np.uint16)
+        b = r.view(np.uint8).reshape(*shape[1:], 2)
+        lo, hi = b[..., 0], b[..., 1]                 # little-endian: bits 0-7, 8-15
+        field = np.full(shape[1:], 8, np.uint8)
+        for edge in _E4M3_EXP_EDGES:
+            field += lo >= np.uint8(edge)
+        code = (field << np.uint8(3)) | (hi & np.uint8(7))
+        code[code == 0x7F] = 0x7E
+        code |= (hi & np.uint8(8)) << np.uint8(4)
+        out[i] = code
+    return out
+
+
+def fp8_block_scales(shape, g: np.random.Generator, base: float = 0.02 / 112) -> np.ndarray:
+    """Per 128x128-block scales around `base` (a factor 2^U(-0.5, 0.5) per block)."""
+    return (base * np.exp2(g.uniform(-0.5, 0.5, size=shape))).astype(np.float32)
+
+
+MLP_WORKLOADS = {
+    "mlp_fp8_M128_E256_k8_H2048_I512": dict(M=128, E=256, k=8, H=2048, I=512),
+}
+
+
+def mlp_inputs(M: int, E: int, k: int, H: int, I: int, seed: int = 0):
+    """Return dict(logits f32 [M,E], x bf16 bits [M,H], w1_q uint8 [E,2I,H] (gate rows then
+    up rows), w1_s f32 [E,2I/128,H/128], w2_q uint8 [E,H,I], w2_s f32 [E,H/128,I/128])."""
+    g = rng(seed)
+    logits = g.standard_normal((M, E), dtype=np.float32)
+    x = bf16_bits(g.standard_normal((M, H), dtype=np.float32))
+    w1_q = fp8_weight_codes((E, 2 * I, H), g)
+    w1_s = fp8_block_scales((E, 2 * I // 128, H // 128), g)
+    w2_q = fp8_weight_codes((E, H, I), g)
+    w2_s = fp8_block_scales((E, H // 128, I // 128), g)
+    return dict(logits=logits, x=x, w1_q=w1_q, w1_s=w1_s, w2_q=w2_q, w2_s=w2_s, M=M, E=E,
+                k=k, H=H, I=I, cap=SOFTCAP)
+
+
 # ---- grouped BF16 GEMM inputs ----------------------------------------------------------
 
 def row_counts(rows: int, E: int, dist: str, g: np.random.Generator) -> np.ndarray:

@@ -65,6 +65,15 @@ def test_workspace_queries(L):
     assert fo == sorted(fo) and all(o % 256 == 0 for o in fo)
     assert fo[-1] < L.moe_ffn_workspace_bytes(64, 8, 2, 512, 256)
     assert L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, 14) == -1
+    mo = [L.moe_mlp_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(16)]
+    mb = L.moe_mlp_workspace_bytes(128, 256, 8, 2048, 512)
+    assert mo == sorted(mo) and all(o % 256 == 0 for o in mo) and mo[-1] < mb
+    # x codes + gate/up rows + act codes + down rows at least
+    assert mb >= R * 2048 + R * 1024 * 4 + R * 512 + R * 2048 * 4
+    assert mo[15] - mo[12] >= R * 1024 * 4 + R * 512 + (512 // 128) * R * 4
+    assert L.moe_mlp_workspace_offset(128, 256, 8, 2048, 512, 16) == -1
+    assert L.moe_mlp_workspace_bytes(128, 256, 8, 2048, 500) == 0                 # I % 128
+    assert L.moe_mlp_workspace_bytes(128, 256, 8, 2000, 512) == 0                 # H % 128
     assert L.moe_gemm_n_tile(0) == 128 and L.moe_gemm_n_tile(1) == 256
     assert L.moe_gemm_n_tile(5) == -1
 
@@ -129,6 +138,18 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw - 1, 0, S) == NOSPC
     assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 300, S) == INVAL   # chunk
     assert ff(P, NULL, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 0, S) == INVAL
+    sq = L.moe_swiglu_quant
+    assert sq(P, 4, 200, P, P, S) == INVAL                                       # I % 128
+    assert sq(P, -1, 256, P, P, S) == INVAL
+    assert sq(NULL, 4, 256, P, P, S) == INVAL
+    mw = L.moe_mlp_workspace_bytes(16, 8, 2, 256, 128)
+    mf = L.moe_mlp_forward
+    assert mf(P, P, P, P, P, P, 16, 8, 2, 256, 128, 30.0, P, P, mw - 1, 0, S) == NOSPC
+    assert mf(P, P, P, P, P, P, 16, 8, 2, 256, 128, 30.0, P, P, mw, 300, S) == INVAL  # chunk
+    assert mf(P, P, P, P, P, P, 16, 8, 2, 256, 100, 30.0, P, P, mw, 0, S) == INVAL    # I % 128
+    assert mf(P, P, P, NULL, P, P, 16, 8, 2, 256, 128, 30.0, P, P, mw, 0, S) == INVAL
+    assert mf(P, P, P, P, P, P, 16, 8, 9, 256, 128, 30.0, P, P, mw, 0, S) == INVAL    # k > E
+    assert mf(P, P, P, P, P, P, 16, 8, 2, 256, 128, float("nan"), P, P, mw, 0, S) == INVAL
 
 
 def test_no_gpu_gives_a_device_status():

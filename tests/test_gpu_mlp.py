@@ -1,0 +1,175 @@
+"""GPU parity of the FP8 expert MLP (moe_swiglu_quant, moe_mlp_forward) against the oracle.
+
+The activation requantiser is bit-exact where silu(g) * u is exact in fp32 (gates far in
+silu's identity range, products of E4M3 values and powers of two, all-zero blocks).  On
+random rows the device forms silu(g) * u in fp32 (two roundings and expf) and the oracle in
+double (one rounding), so a code may land one E4M3 step away where the value sits on a
+rounding boundary: scales are held to a few fp32 ulps and the dequantised values to one E4M3
+step, with at most 1 % of codes differing.
+
+The layer output is held to the BF16 output bar in aggregate (relative Frobenius 5e-3), but not
+element by element: the first GEMM's fp32 rows carry the matrix core's ~2^-13 per-block
+error, so about 0.2 % of the activation codes land one E4M3 step (<= 2^-3 of the value) away
+from the oracle's, and each such flip moves every output of its route by that step times the
+weight.  One flip changes an output by at most 2^-3 * (|a|/rms a) * (|w|/rms w) / sqrt(I) of
+its rms: with |a| <= 8 rms, |w| <= 448/123 rms and I >= 256 that is <= 0.23, and 0.15 covers
+the combine over k routes of unit-sum weights in practice.  So elements are held to 2e-2 rms
+for all but 0.5 % of them and to 0.15 rms everywhere (MLP_*).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mixture_experts_layer_softcap_amd import moe, synth
+
+from gpu_util import REL_FRO, bf16_f64, to_dev, to_np, zeros
+
+pytestmark = pytest.mark.gpu
+
+CAP = synth.SOFTCAP
+MLP_ELEM_RMS = 2e-2          # per-element bar for all but MLP_OUTLIER_FRAC of the elements
+MLP_OUTLIER_FRAC = 5e-3
+MLP_MAX_RMS = 0.15           # every element
+
+
+def assert_mlp_close(y_bits, ref64, what=""):
+    assert_bf16_close_fro(y_bits, ref64, what)
+    y = bf16_f64(y_bits)
+    ref = np.asarray(ref64, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    d = np.abs(y - ref)
+    frac = float((d > MLP_ELEM_RMS * rms).mean())
+    assert frac <= MLP_OUTLIER_FRAC, f"{what}: {frac:.4f} of elements beyond {MLP_ELEM_RMS} rms"
+    assert d.max() <= MLP_MAX_RMS * rms, f"{what}: max |d| {d.max():.3e} vs rms {rms:.3e}"
+
+
+def assert_bf16_close_fro(y_bits, ref64, what=""):
+    y = bf16_f64(y_bits)
+    ref = np.asarray(ref64, np.float64)
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    fro = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert fro <= REL_FRO, f"{what}: relative Frobenius error {fro:.3e} > {REL_FRO}"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc.build(force=False)
+    assert moe.device_check() == moe.MOE_OK
+
+
+def gpu_swiglu_quant(h):
+    rows, I2 = h.shape
+    I = I2 // 2
+    a_q = zeros((rows, I), torch.uint8)
+    a_s = zeros((I // 128, rows), torch.float32)
+    moe.swiglu_quant(to_dev(h.astype(np.float32)), a_q, a_s)
+    torch.cuda.synchronize()
+    return to_np(a_q), to_np(a_s)
+
+
+def oracle_swiglu_quant(h):
+    act = orc.swiglu_f32(h.astype(np.float64))
+    return orc.quant_rows_f32(act)
+
+
+@pytest.mark.parametrize("I", [128, 384, 640])
+def test_swiglu_quant_exact_rows(I):
+    g = np.random.default_rng(I)
+    rows = 37
+    vals = np.array([0.0, 1.0, 0.5, 0.25, 0.75, 1.5, 3.0, 0.125, 0.0625, 448.0], np.float32)
+    gate = g.choice(np.array([64.0, 128.0, 256.0, 1024.0], np.float32), (rows, I))
+    up = g.choice(vals, (rows, I)) * g.choice(np.array([-1, 1], np.float32), (rows, I))
+    up *= np.exp2(g.integers(-6, 4, (rows, 1))).astype(np.float32)
+    gate[3, :] = 0.0                                  # act = +-0: scale 0, signed zero codes
+    up[3, :] = np.where(np.arange(I) % 2, -1.0, 2.0)
+    gate[5, 128:256 if I > 128 else 128] = 0.0        # one zero block inside a live row
+    h = np.concatenate([gate, up], axis=1)
+    q, s = gpu_swiglu_quant(h)
+    rq, rs = oracle_swiglu_quant(h)
+    np.testing.assert_array_equal(s.T.view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(q, rq)
+    assert rs[3].tolist() == [0.0] * (I // 128)
+    assert set(np.unique(q[3]).tolist()) <= {0x00, 0x80}
+
+
+@pytest.mark.parametrize("rows,I", [(1, 128), (53, 512), (200, 1536)])
+def test_swiglu_quant_random_rows(rows, I):
+    g = np.random.default_rng(rows + I)
+    h = (g.standard_normal((rows, 2 * I)) * 2.0).astype(np.float32)
+    q, s = gpu_swiglu_quant(h)
+    rq, rs = oracle_swiglu_quant(h)
+    s = s.T
+    np.testing.assert_allclose(s, rs, rtol=5e-7, atol=0)
+    dq = orc.e4m3_decode_table()
+    got = dq[q] * np.repeat(s.astype(np.float64), 128, 1)
+    ref = dq[rq] * np.repeat(rs.astype(np.float64), 128, 1)
+    step = 2.0 ** -3 * np.abs(ref) + 2.0 ** -9 * np.repeat(rs.astype(np.float64), 128, 1)
+    assert (np.abs(got - ref) <= step * 1.0001).all()
+    assert (q != rq).mean() <= 0.01
+
+
+def test_swiglu_quant_zero_rows_is_a_no_op():
+    a_q = zeros((1, 128), torch.uint8)
+    a_s = zeros((1, 1), torch.float32)
+    h = zeros((0, 256), torch.float32)
+    moe.swiglu_quant(h, a_q, a_s)
+    torch.cuda.synchronize()
+    assert int(a_q.sum()) == 0 and float(a_s.sum()) == 0.0
+
+
+def gpu_mlp(d, chunk=0, reps=1):
+    M, H = d["x"].shape
+    E, k, I = d["E"], d["k"], d["I"]
+    args = [to_dev(d[n]) for n in ("logits", "x", "w1_q", "w1_s", "w2_q", "w2_s")]
+    ws = zeros(moe.mlp_workspace_bytes(M, E, k, H, I), torch.uint8)
+    outs = []
+    for _ in range(reps):
+        out = zeros((M, H), torch.int16)
+        moe.mlp_forward(*args, k, CAP, out, ws, chunk_rows=chunk)
+        torch.cuda.synchronize()
+        outs.append(to_np(out, np.uint16))
+    return outs, ws
+
+
+def ws_part(ws, d, which, dtype, n):
+    M, H = d["x"].shape
+    off = moe.mlp_workspace_offset(M, d["E"], d["k"], H, d["I"], which)
+    size = np.dtype(dtype).itemsize * n
+    return to_np(ws[off:off + size]).view(dtype)
+
+
+@pytest.mark.parametrize("M,E,k,H,I,chunk", [
+    (8, 16, 2, 256, 256, 0),       # the correctness-sized layer; general GEMM for both
+    (37, 5, 3, 384, 384, 64),      # ragged segments, 64-row chunks
+    (64, 8, 2, 2048, 512, 16),     # streaming range GEMM (K = 2048) then the general one
+    (64, 8, 2, 2048, 512, 128),    # LDS-tiled GEMM for both projections
+])
+def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk):
+    d = synth.mlp_inputs(M, E, k, H, I, seed=M + H)
+    outs, ws = gpu_mlp(d, chunk=chunk, reps=2)
+    _, y64 = orc.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
+                            k, CAP)
+    assert_mlp_close(outs[0], y64, f"mlp M={M} H={H} I={I} chunk={chunk}")
+    np.testing.assert_array_equal(outs[1], outs[0])
+    ids, _ = orc.route(d["logits"], k, CAP)
+    counts, offsets = orc.layout(ids, E)
+    np.testing.assert_array_equal(ws_part(ws, d, 0, np.int32, M * k).reshape(M, k), ids)
+    np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, E), counts)
+    np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), offsets)
+
+
+def test_mlp_forward_full_size_sampled():
+    # the FP8 tutorial's layer as a full expert MLP: M=128, 256 experts, top-8, hidden 2048,
+    # expert width 512 (gate+up 1024 columns)
+    d = synth.mlp_inputs(**{kk: v for kk, v in
+                            synth.MLP_WORKLOADS["mlp_fp8_M128_E256_k8_H2048_I512"].items()})
+    outs, _ = gpu_mlp(d, reps=2)
+    g = np.random.default_rng(0)
+    toks = np.unique(np.concatenate([[0, d["M"] - 1], g.choice(d["M"], 14, replace=False)]))
+    _, y64 = orc.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
+                            d["k"], CAP, tokens=toks.astype(np.int32))
+    assert_mlp_close(outs[0][toks], y64, "mlp full size")
+    np.testing.assert_array_equal(outs[1], outs[0])
