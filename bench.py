@@ -241,6 +241,131 @@ def bench_ffn(args, moe, synth, torch, np):
     print(json.dumps(result))
 
 
+def bench_mlp(args, moe, synth, torch, np):
+    """--workload mlp_fp8_M<M>_E<E>_k<k>_H<H>_I<I>: the whole FP8 expert MLP layer per step
+    (route, layouts, QSG, gate+up FP8 GEMM, silu(g)*u requantise, down FP8 GEMM, combine);
+    the dominant kernel, the gate+up GEMM, is also timed alone on the step's own inputs."""
+    d = synth.mlp_inputs(**synth.MLP_WORKLOADS[args.workload])
+    M, E, k, H, I, cap = d["M"], d["E"], d["k"], d["H"], d["I"], d["cap"]
+    dev = torch.device("cuda:0")
+    tl = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    logits, x = tl(d["logits"]), tl(d["x"])
+    w1 = (tl(d["w1_q"]), tl(d["w1_s"]))
+    w2 = (tl(d["w2_q"]), tl(d["w2_s"]))
+    wbytes = w1[0].numel() + w2[0].numel()
+    copies = max(1, -(-WEIGHT_BYTES_ROTATION // wbytes))
+    w1s = [w1] + [(w1[0].clone(), w1[1].clone()) for _ in range(copies - 1)]
+    w2s = [w2] + [(w2[0].clone(), w2[1].clone()) for _ in range(copies - 1)]
+    out = torch.empty((M, H), dtype=torch.int16, device=dev)
+    ws = torch.empty(moe.mlp_workspace_bytes(M, E, k, H, I), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        a, b = w1s[i % copies], w2s[i % copies]
+        moe.mlp_forward(logits, x, a[0], a[1], b[0], b[1], k, cap, out, ws,
+                        chunk_rows=args.chunk_rows)
+
+    for i in range(max(args.warmup, copies)):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+
+    # the gate+up GEMM alone on the sorted FP8 rows, tasks and ids the last step left
+    def wsp(i, dtype, n):
+        o = moe.mlp_workspace_offset(M, E, k, H, I, i)
+        return ws[o:o + n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+
+    R = M * k
+    chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if H <= 8192 else 64))
+    mtu = moe.max_tasks(M, k, E, 2 * I // 128, chunk)
+    a_q = wsp(10, torch.uint8, R * H).view(R, H)
+    a_s = wsp(11, torch.float32, (H // 128) * R)
+    tasks = wsp(5, torch.int32, 4 * mtu).view(mtu, 4)
+    nt = wsp(7, torch.int32, 1)
+    o7 = moe.mlp_workspace_offset(M, E, k, H, I, 7)
+    queue = ws[o7 + 16:o7 + 24].view(torch.int32)
+    sorted_ids = wsp(8, torch.int32, R)
+    h1 = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
+
+    def gemm(i):
+        a = w1s[i % copies]
+        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, a[0], a[1], tasks, nt, chunk, h1,
+                         moe.MOE_EPI_STORE_F32, queue=queue, sorted_route_ids=sorted_ids)
+
+    for i in range(2 * copies):
+        gemm(i)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(args.steps):
+        gemm(i)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gemm_us = g0.elapsed_time(g1) * 1e3 / args.steps
+
+    ids_np = wsp(0, torch.int32, R).cpu().numpy()
+    counts = np.bincount(ids_np, minlength=E)
+    nonempty = int((counts > 0).sum())
+    N1 = 2 * I
+    gbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4) + R * H + (H // 128) * R * 4 \
+        + R * 4 + R * N1 * 4
+    achieved = gbytes / (gemm_us * 1e-6) / 1e9
+    lbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4) \
+        + M * E * 4 + M * H * 2 + M * H * 2
+    flops = 2.0 * R * (N1 * H + H * I)
+    gemm_kernel = ("gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
+                   if H == 2048 and chunk <= 16 else
+                   "gemm_fp8_tile_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
+                   if 64 < chunk <= 256 and H <= 8192 else
+                   "gemm_fp8_kernel (gate+up grouped FP8 GEMM, STORE_F32)")
+    result = {
+        "metric": "µs/layer + effective TFLOPS & %HBM roofline, FP8 expert MLP",
+        "value": round(us, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "H": H, "I": I,
+                   "softcap": cap, "weight_copies_rotated": copies, "chunk_rows": chunk,
+                   "path": "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "
+                           "silu*up requantise, down GEMM, combine"},
+        "effective_tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "layer_hbm_frac": round(lbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_algorithmic_bytes": lbytes,
+        "nonempty_experts": nonempty,
+        "roofline": {"bound": "hbm", "kernel": gemm_kernel,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" ")[0]),
+                     "algorithmic_bytes_per_launch": gbytes,
+                     "avg_launch_us": round(gemm_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=not os.path.exists(oracle.LIB_PATH))
+        times = []
+        t_end = time.perf_counter() + 12.0
+        while time.perf_counter() < t_end or len(times) < 2:
+            t0 = time.perf_counter()
+            oracle.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
+                              k, cap)
+            times.append(time.perf_counter() - t0)
+        result["cpu_baseline"] = {
+            "value": statistics.median(times) * 1e6, "unit": "us/layer", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole layer ({M} tokens, fp64 single-threaded C oracle), median of "
+                      f"{len(times)} runs; host has {os.cpu_count()} cores"}
+    print(json.dumps(result))
+
+
 def staged_gemm(args, moe, torch, wsp, M, E, k, K, N, chunk, wqs, wss, copies, rows_out):
     """The staged step's grouped GEMM alone (ROUTE_F32 epilogue) on the task list, FP8 rows and
     scales the last staged forward left in the workspace."""
@@ -292,6 +417,9 @@ def main():
         return
     if args.workload.startswith("ffn_mixtral_"):
         bench_ffn(args, moe, synth, torch, np)
+        return
+    if args.workload.startswith("mlp_fp8_"):
+        bench_mlp(args, moe, synth, torch, np)
         return
     d = synth.workload_inputs(args.workload)
     M, E, k, K, N, cap = d["M"], d["E"], d["k"], d["K"], d["N"], d["cap"]
@@ -393,7 +521,7 @@ def main():
                        "token-major rows, ROUTE_F32)")
     elif fused:
         gemm_kernel = "gemm_fp8_fused_kernel (grouped FP8 GEMM from routed ids, rows at route ids)"
-    elif K == 2048 and chunk <= 16:
+    elif K in (512, 1024, 2048) and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
     elif 64 < chunk <= 256 and K <= 8192:
         gemm_kernel = "gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles, ROUTE_F32)"
@@ -422,7 +550,7 @@ def main():
                             else "5 kernels: route, layout, QSG, grouped GEMM, combine"),
                    "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
                                       else "contiguous ranges, per-wave pull"
-                                      if K == 2048 and chunk <= 16
+                                      if K in (512, 1024, 2048) and chunk <= 16
                                       else "one task per workgroup, chunks spread over XCDs"
                                       if 64 < chunk <= 256 and K <= 8192
                                       else "static stride" if args.static_grid else "atomic queue"),

@@ -168,9 +168,9 @@ int moe_gemm_n_tile(int mode);
  * the task's 128 columns c (weight rows [0, N/2) are the gate, [N/2, N) the up projection).
  * One 256 x 256 output tile per task and workgroup (grid = max_tasks; workgroups past
  * *ntasks exit at once); queue is not used.
- * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 2048 the task list is cut into one
- * contiguous range of 16-column subtasks per workgroup, balanced inside the workgroup by an
- * LDS counter; queue is not used.  For chunk_rows in [65, 256] (K <= 8192) one workgroup
+ * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 512, 1024 or 2048 the task list is
+ * cut into one contiguous range of 16-column subtasks per workgroup, balanced inside the
+ * workgroup by an LDS counter; queue is not used.  For chunk_rows in [65, 256] (K <= 8192) one workgroup
  * runs one task with both operands staged in LDS (grid = max_tasks rounded up to whole
  * chunks per XCD; workgroups past *ntasks exit at once; the panels of one chunk run on one
  * XCD); queue is not used.  Otherwise, with queue != NULL, a persistent grid pulls
@@ -318,7 +318,8 @@ int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_sca
  * 5 gate+up tasks, 6 down tasks, 7 ntasks (gate+up, down) at +0 and queue pairs at +16,
  * 8 sorted_route_ids, 9 route_slots, 10 x codes (sorted), 11 x scales, 12 gate+up rows f32
  * [M*k][2I], 13 act codes [M*k][I], 14 act scales [I/128][M*k], 15 down rows f32 [M*k][H]
- * at route ids.  Eight plain launches on `stream`, no host synchronisation. */
+ * at route ids.  Seven plain launches on `stream` (one layout pass writes both task lists),
+ * no host synchronisation. */
 size_t moe_mlp_workspace_bytes(int M, int E, int k, int H, int I);
 int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which);
 int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,

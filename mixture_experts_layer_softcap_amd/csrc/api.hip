@@ -700,10 +700,8 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
-        (e = launch_layout(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu, mtu, nt,
-                           queue, nullptr, nullptr, s)) != hipSuccess ||
-        (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
-                           nt + 1, queue + 2, nullptr, nullptr, s)) != hipSuccess ||
+        (e = launch_layout2(ids, M, k, E, chunk, counts, offsets, cursors, nbu, tu, nt, queue,
+                            nbd, td, nt + 1, queue + 2, s)) != hipSuccess ||
         (e = launch_qsg(x, M, H, ids, k, E, cursors, sorted, slots, xq, xs, s)) != hipSuccess ||
         (e = launch_gemm_fp8(xq, xs, R, H, w1_q, w1_scales, E, 2 * I, tu, nt, mtu, chunk, queue,
                              MOE_EPI_STORE_F32, sorted, h1, s)) != hipSuccess ||

@@ -1,4 +1,5 @@
-// gemm_fp8_range.hip -- grouped FP8 GEMM for tasks of at most 16 routed rows and K = 2048: the
+// gemm_fp8_range.hip -- grouped FP8 GEMM for tasks of at most 16 routed rows and K = 512, 1024
+// or 2048: the
 // small-batch regime of the pages ([FMF8] problem table, about 4 rows per expert; Baseline
 // item 6 with per-K-block scaling; [WEAVE] sections 2.2 and 4.2 for the persistent walk over a
 // task list).
@@ -13,14 +14,15 @@
 //
 // Routed rows.  Each chunk's rows (16 x K bytes, the MFMA B operand, shared by all 8 waves)
 // and their block scales go from global memory straight into LDS (global_load_lds), in MFMA
-// fragment order, for every chunk of the range at once when they fit (4 at K = 2048;
+// fragment order, for every chunk of the range at once when they fit (4 at K = 2048, 16 at
+// K = 512;
 // otherwise in rounds).  Wave 0 scans the range and moves the tiles before its own weight
 // loads; the barrier that publishes them leaves every wave's first weight burst in flight.
 // There is no barrier per task.
 //
 // Weights.  A subtask is read as units of one k-block (16 rows x 128 bytes: two 16-byte loads
 // per lane, lane (j, g) holding bytes [g*16, g*16+16) and [64+g*16, 80+g*16) of row j).  A ring
-// of MOE_RANGE_RING units lives in registers; each unit is refilled right after its MFMA has
+// of min(MOE_RANGE_RING, K/128) units lives in registers; each unit is refilled right after its MFMA has
 // consumed it, with the same k-block of the next pass or of the next subtask, so a wave keeps
 // the ring's loads in flight through subtask boundaries.  Weights carry the non-temporal hint.
 // Measured on MI355X with this grid: the weight stream alone runs at 6.1 TB/s in this order
@@ -44,7 +46,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRing = MOE_RANGE_RING;           // k-block units per wave in registers
+constexpr int kRingMax = MOE_RANGE_RING;        // k-block units per wave in registers
 constexpr int kTileBudget = 136 * 1024;         // LDS bytes for routed-row tiles
 
 struct TaskD {
@@ -102,16 +104,17 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ a,
 
 
 // NT: weights are read with the non-temporal hint (streamed once, kept out of the caches).
-template <int KB2, int EPI, bool NT>
+template <int KB, int EPI, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_range_kernel(const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
                            const uint8_t* w, const float* __restrict__ w_scales,
                            const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                            const int32_t* __restrict__ sorted_ids, void* __restrict__ out,
                            int rows, int N) {
-    constexpr int K = 2048 * KB2;
-    constexpr int KB = K / 128;
+    constexpr int K = KB * 128;
+    constexpr int kRing = KB < kRingMax ? KB : kRingMax;
     constexpr int P = KB / kRing;               // passes of the ring per subtask
+    static_assert(KB % kRing == 0 && KB % 4 == 0, "K: a multiple of 512 and of the ring");
     constexpr int MAXT = TileLds<KB>::kMax;
     static_assert(MAXT >= 1, "one tile must fit");
     __shared__ TileLds<KB> L;
@@ -319,7 +322,7 @@ void gemm_fp8_range_kernel(const uint8_t* __restrict__ a, const float* __restric
     }
 }
 
-template <int KB2, bool NT>
+template <int KB, bool NT>
 hipError_t launch_kr(const uint8_t* a, const float* a_scales, int rows, const uint8_t* w,
                      const float* w_scales, int N, const moe_task* tasks,
                      const int32_t* ntasks, int epilogue, const int32_t* sorted, void* out,
@@ -327,17 +330,17 @@ hipError_t launch_kr(const uint8_t* a, const float* a_scales, int rows, const ui
     const int4* t = reinterpret_cast<const int4*>(tasks);
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB2, MOE_EPI_STORE_BF16, NT>),
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_BF16, NT>),
                                dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
                                ntasks, sorted, out, rows, N);
             break;
         case MOE_EPI_ROUTE_F32:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB2, MOE_EPI_ROUTE_F32, NT>),
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_ROUTE_F32, NT>),
                                dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
                                ntasks, sorted, out, rows, N);
             break;
         default:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB2, MOE_EPI_STORE_F32, NT>),
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_F32, NT>),
                                dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
                                ntasks, sorted, out, rows, N);
     }
@@ -352,7 +355,7 @@ hipError_t launch_kr(const uint8_t* a, const float* a_scales, int rows, const ui
 
 bool gemm_fp8_range_applies(int K, int chunk_rows) {
     // K = 4096 needs more registers than two waves per SIMD leave (it spills)
-    return chunk_rows <= 16 && K == 2048;
+    return chunk_rows <= 16 && (K == 512 || K == 1024 || K == 2048);
 }
 
 hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int rows, int K,
@@ -363,9 +366,15 @@ hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int ro
     int grid = device_info().cu_count;          // one 8-wave workgroup per CU
     if (grid > max_tasks) grid = max_tasks;
     if (grid <= 0) return hipSuccess;
-    (void)K;  // 2048 (gemm_fp8_range_applies)
-    return launch_kr<1, MOE_RANGE_NT != 0>(a, a_scales, rows, w, w_scales, N, tasks, ntasks,
-                                          epilogue, sorted, out, grid, s);
+    constexpr bool nt = MOE_RANGE_NT != 0;
+    if (K == 512)
+        return launch_kr<4, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
+                                sorted, out, grid, s);
+    if (K == 1024)
+        return launch_kr<8, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
+                                sorted, out, grid, s);
+    return launch_kr<16, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
+                             sorted, out, grid, s);
 }
 
 }  // namespace moe

@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
     const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
     moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue,
-    int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots) {
+    int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots, int n_blocks2,
+    moe_task* __restrict__ tasks2, int32_t* __restrict__ ntasks2, uint32_t* __restrict__ queue2) {
     // one histogram per wave over its own contiguous range of routes: the LDS atomics of a
     // busy expert are spread over 16 counters instead of queueing on one
     __shared__ int s_hw[kWaves][kThreads];
@@ -139,6 +140,14 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
     const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
     write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
                 s_wsum);
+    if (tasks2) {
+        // a second task list over the same chunks, n_blocks2 panels each
+        __syncthreads();
+        s_hist[tid] = 0;
+        __syncthreads();
+        write_tasks(c, row0, E, n_blocks2, chunk, offsets, cursors, tasks2, ntasks2, queue2,
+                    s_hist, s_wsum);
+    }
     if (tid < E) {
         counts[tid] = c;
         // each wave's first slot inside the expert's segment (waves in route order)
@@ -259,7 +268,17 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
     (void)max_tasks;  // capacity checked on the host against moe_max_tasks
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
                        chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
-                       sorted_route_ids, route_slots);
+                       sorted_route_ids, route_slots, 0, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout2(const int32_t* ids, int M, int k, int E, int chunk_rows,
+                          int32_t* counts, int32_t* offsets, int32_t* cursors, int n_blocks,
+                          moe_task* tasks, int32_t* ntasks, uint32_t* queue, int n_blocks2,
+                          moe_task* tasks2, int32_t* ntasks2, uint32_t* queue2, hipStream_t s) {
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
+                       chunk_rows, counts, offsets, cursors, tasks, ntasks, queue, nullptr,
+                       nullptr, n_blocks2, tasks2, ntasks2, queue2);
     return hipGetLastError();
 }
 

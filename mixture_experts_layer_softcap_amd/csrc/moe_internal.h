@@ -42,6 +42,12 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
                          int max_tasks, int32_t* ntasks, uint32_t* queue,
                          int32_t* sorted_route_ids, int32_t* route_slots, hipStream_t s);
 
+// one layout pass writing two task lists over the same chunks (n_blocks and n_blocks2 panels)
+hipError_t launch_layout2(const int32_t* ids, int M, int k, int E, int chunk_rows,
+                          int32_t* counts, int32_t* offsets, int32_t* cursors, int n_blocks,
+                          moe_task* tasks, int32_t* ntasks, uint32_t* queue, int n_blocks2,
+                          moe_task* tasks2, int32_t* ntasks2, uint32_t* queue2, hipStream_t s);
+
 hipError_t launch_qsg(const uint16_t* x, int M, int K, const int32_t* ids, int k, int E,
                       int32_t* cursors, int32_t* sorted_route_ids, int32_t* route_slots,
                       uint8_t* a_q, float* a_scales, hipStream_t s);

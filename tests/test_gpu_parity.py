@@ -348,10 +348,13 @@ def gpu_gemm(a_q, a_s, w_q, w_s, offsets, chunk, epilogue, sorted_ids=None, queu
                                            (16, False, 2048), (7, False, 4096),
                                            (3, True, 4096), (64, False, 2048),
                                            (128, True, 512), (256, False, 2048),
-                                           (200, True, 4096), (256, True, 128)])
+                                           (200, True, 4096), (256, True, 128),
+                                           (16, True, 1024), (16, True, 640),
+                                           (9, False, 768)])
 def test_gemm_integer_exact(chunk, queue, K):
-    # K in {2048, 4096} with chunk <= 16 takes the streaming kernel, chunks of 65..256 rows the
-    # LDS-tiled kernel, the rest the general one
+    # K in {512, 1024, 2048} with chunk <= 16 takes the streaming range kernel, chunks of
+    # 65..256 rows the LDS-tiled kernel, the rest (K = 640, 768, 4096 at small chunks, and
+    # chunks of 17..64 rows) the general one
     g = np.random.default_rng(chunk + K)
     E, N = 4, 256
     counts = np.array([3, 0, 37, 70], np.int32)
