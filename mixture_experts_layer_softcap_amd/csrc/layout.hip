@@ -40,14 +40,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& tot
     return excl;
 }
 
+// chunks whose tasks are written from an LDS table, consecutive threads on consecutive tasks
+constexpr int kChunkTable = 4096;
+
 // The task list of expert counts c (thread e holds c_e and its exclusive prefix row0): full
 // chunk_rows-row chunks first (expert order), then the partial chunks by a counting sort on
 // their row count, largest first, each crossed with the n_blocks panels; also offsets[E+1],
 // cursors = offsets, ntasks, and the queue reset.  Every thread of the workgroup calls it.
+// Up to kChunkTable chunks, each expert's thread only files its chunks in LDS and the whole
+// workgroup then writes the tasks in order (every store instruction covers 1 KiB of the
+// list); beyond that, each expert's thread writes its own tasks.
 __device__ void write_tasks(int c, int row0, int E, int n_blocks, int chunk,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
                             moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks,
                             uint32_t* __restrict__ queue, int* s_hist, int* s_wsum) {
+    __shared__ int2 s_chunks[kChunkTable];        // (row_begin, expert | rows << 16)
     const int tid = threadIdx.x;
     const int full = c / chunk;
     const int tail = c - full * chunk;
@@ -62,10 +69,29 @@ __device__ void write_tasks(int c, int row0, int E, int n_blocks, int chunk,
     const int larger = block_exclusive_scan(h, s_wsum, total_tails);
     if (size >= 1) s_hist[size] = larger;                 // first position of size `size`
     __syncthreads();
+    const int nchunks = total_full + total_tails;
     if (tid < E) {
         offsets[tid] = row0;
         cursors[tid] = row0;
         if (tid == E - 1) offsets[E] = row0 + c;
+    }
+    if (nchunks <= kChunkTable) {                         // uniform over the workgroup
+        if (tid < E) {
+            for (int i = 0; i < full; ++i)
+                s_chunks[full0 + i] = make_int2(row0 + i * chunk, tid | (chunk << 16));
+            if (tail > 0)
+                s_chunks[total_full + atomicAdd(&s_hist[tail], 1)] =
+                    make_int2(row0 + full * chunk, tid | (tail << 16));
+        }
+        __syncthreads();
+        const int T = nchunks * n_blocks;
+        for (int t = tid; t < T; t += kThreads) {
+            const int p = t / n_blocks;
+            const int2 ci = s_chunks[p];
+            *reinterpret_cast<int4*>(&tasks[t]) =
+                make_int4(ci.y & 0xFFFF, ci.x, ci.y >> 16, t - p * n_blocks);
+        }
+    } else if (tid < E) {
         for (int i = 0; i < full; ++i) {
             const int p = full0 + i;
             for (int nb = 0; nb < n_blocks; ++nb)
@@ -80,7 +106,7 @@ __device__ void write_tasks(int c, int row0, int E, int n_blocks, int chunk,
         }
     }
     if (tid == 0) {
-        ntasks[0] = (total_full + total_tails) * n_blocks;
+        ntasks[0] = nchunks * n_blocks;
         queue[0] = 0u;
         queue[1] = 0u;
     }
