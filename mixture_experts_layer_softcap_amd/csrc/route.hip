@@ -9,11 +9,14 @@
 // ballot per register for the lowest-index holder of that maximum, which is retired.  tanh
 // and exp run only for the k winners, on lanes 0..k-1.
 //
-// With QUANT the wave also quantises its token's row of x once, with the rule of the
+// With QUANT the token's row of x is also quantised once, with the rule of the
 // quantise-sort-gather stage ([FMF8] Baseline items 4-5: amax per 128-value block, scale =
 // amax/448, E4M3 of x times the reciprocal), into token-major codes [M][K] and scales
 // [K/128][M]: the grouped GEMM then gathers each routed row from there by its token instead
-// of reading a sorted copy of it (one copy per token, not one per route).
+// of reading a sorted copy of it (one copy per token, not one per route).  Routing and
+// quantisation are independent, so they run in different waves (grid row 0 routes, rows
+// 1..kQuantSplit quantise one slice of K each): a wave's serial chain, not bandwidth, sets
+// this kernel's time.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -21,6 +24,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteWaves = 4;   // tokens (waves) per workgroup at most
+constexpr int kQuantSplit = 2;   // waves quantising one token's row, each a slice of K
 
 // monotone 32-bit image of a logit (the high word of route_key)
 __device__ __forceinline__ uint32_t logit_ord(float v) { return (uint32_t)(route_key(v, 0) >> 32); }
@@ -51,6 +55,37 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales, int32_t* __restrict__ zero0,
     int32_t* __restrict__ zero1, int zero_n) {
     const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (QUANT && blockIdx.y > 0) {
+        // quantisation of token t's slice blockIdx.y - 1 of K (whole 128-value blocks); 512
+        // values per pass: lane l holds values [8l, 8l+8) of the pass, so a 128-value block
+        // is an aligned group of 16 lanes, wholly inside or outside the slice
+        if (t >= M) return;
+        const int per = (K / 128 + kQuantSplit - 1) / kQuantSplit * 128;
+        const int k_lo = (blockIdx.y - 1) * per;
+        const int k_hi = min(K, k_lo + per);
+        constexpr int kPasses = 2;
+        for (int base = k_lo; base < k_hi; base += kPasses * 512) {
+            uint4 xr[kPasses];
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                const int k0 = base + q * 512 + lane * 8;
+                xr[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (k0 < k_hi) xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0);
+            }
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                const int k0 = base + q * 512 + lane * 8;
+                const bool valid = k0 < k_hi;
+                const Quant8 qv = quantise8(xr[q], valid);
+                if (valid) {
+                    *reinterpret_cast<uint2*>(x_q + (size_t)t * K + k0) = qv.codes;
+                    if ((lane & 15) == 0) x_scales[(size_t)(k0 >> 7) * M + t] = qv.scale;
+                }
+            }
+        }
+        return;
+    }
     // scratch the next kernels accumulate into (per-expert counts and cursors)
     if (zero0 && blockIdx.x == 0) {
         for (int i = threadIdx.x; i < zero_n; i += blockDim.x) {
@@ -58,19 +93,8 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
             zero1[i] = 0;
         }
     }
-    const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= M) return;
     const float* row = logits + (size_t)t * E;
-    // the token's first 2048 values of x (four passes of 512) are requested before the
-    // routing work
-    constexpr int kPasses = 4;
-    uint4 xr[kPasses];
-#pragma unroll
-    for (int q = 0; q < kPasses; ++q) {
-        xr[q] = make_uint4(0u, 0u, 0u, 0u);
-        if (QUANT && q * 512 + lane * 8 < K)
-            xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + q * 512 + lane * 8);
-    }
 
     float val[VPL];
     uint32_t ord[VPL];
@@ -124,31 +148,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         ids[(size_t)t * k + lane] = my_e;
         weights[(size_t)t * k + lane] = ex / sum;
     }
-    if (QUANT) {
-        // 512 values per pass: lane l holds values [8l, 8l+8) of the pass, so a 128-value
-        // block is an aligned group of 16 lanes (K is a multiple of 128: a group is wholly
-        // inside or outside the row); passes go in groups of four, loads first
-        for (int base = 0;;) {
-#pragma unroll
-            for (int q = 0; q < kPasses; ++q) {
-                const int k0 = base + q * 512 + lane * 8;
-                const bool valid = k0 < K;
-                const Quant8 qv = quantise8(xr[q], valid);
-                if (valid) {
-                    *reinterpret_cast<uint2*>(x_q + (size_t)t * K + k0) = qv.codes;
-                    if ((lane & 15) == 0) x_scales[(size_t)(k0 >> 7) * M + t] = qv.scale;
-                }
-            }
-            base += kPasses * 512;
-            if (base >= K) break;
-#pragma unroll
-            for (int q = 0; q < kPasses; ++q) {
-                const int k0 = base + q * 512 + lane * 8;
-                xr[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (k0 < K) xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0);
-            }
-        }
-    }
 }
 
 template <int VPL>
@@ -158,8 +157,8 @@ hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, i
     const int per = M >= kRouteWaves * device_info().cu_count ? kRouteWaves : 1;
     const int grid = (M + per - 1) / per;
     if (x_q)
-        hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid), dim3(64 * per), 0, s,
-                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
+        hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid, 1 + kQuantSplit),
+                           dim3(64 * per), 0, s, logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
                            z1, zn);
     else
         hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * per), 0, s,
