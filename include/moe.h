@@ -275,17 +275,18 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
 /* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------
- * route (softcap, top-k) -> layout (chunk_rows rows per task, 0 = 256) -> bf16 sort+gather
- * -> gated-up grouped GEMM with the SwiGLU epilogue -> down grouped GEMM (fp32 rows) ->
- * routing-weighted combine:
+ * route (softcap, top-k) -> layout over many workgroups (chunk_rows rows per task, 0 = 256;
+ * sorted route ids, route -> slot, both task lists) -> gated-up grouped GEMM reading each
+ * routed row straight from x (gathered on load) with the SwiGLU epilogue -> down grouped GEMM
+ * (fp32 rows) -> routing-weighted combine:
  *   act[r] = bf16(silu(x[t] . w_up[e][0:F]^T) * (x[t] . w_up[e][F:2F]^T)),
  *   y[t] = bf16( sum_j w_tj * act[r_j] . w_down[e_j]^T )      (fp32 accumulation)
  * logits f32 [M][E], x bf16 [M][H], w_up bf16 [E][2F][H] (gate rows then up rows),
  * w_down bf16 [E][H][F] -> out bf16 [M][H].  H a multiple of 256, F of 128.  Workspace of
  * moe_ffn_workspace_bytes(...) bytes; parts (for inspection): 0 topk_ids, 1 topk_weights,
  * 2 counts, 3 offsets, 4 cursors, 5 up tasks, 6 down tasks, 7 ntasks, 8 sorted_route_ids,
- * 9 route_slots, 10 gathered rows, 11 act, 12 down rows, 13 queue counters.  Seven plain
- * launches on `stream`, no host synchronisation. */
+ * 9 route_slots, 10 per-expert slot cursors of the layout, 11 act, 12 down rows, 13 queue
+ * counters.  Six plain launches on `stream`, no host synchronisation. */
 size_t moe_ffn_workspace_bytes(int M, int E, int k, int H, int F);
 int64_t moe_ffn_workspace_offset(int M, int E, int k, int H, int F, int which);
 int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up,

@@ -274,7 +274,7 @@ FfnLayout ffn_layout(int M, int E, int k, int H, int F) {
         16,                        // 7 ntasks (up, down) and two queue pairs
         R * 4,                     // 8 sorted_route_ids
         R * 4,                     // 9 route_slots
-        R * (size_t)H * 2,         // 10 gathered rows, bf16 [R][H]
+        (size_t)E * 4,             // 10 per-expert slot cursors of the wide layout
         R * (size_t)F * 2,         // 11 act = silu(gate) * up, bf16 [R][F]
         R * (size_t)H * 4,         // 12 down-projection rows, f32 [R][H]
         16,                        // 13 queue counters
@@ -611,7 +611,7 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
     int32_t* nt = reinterpret_cast<int32_t*>(at(7));
     int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
     int32_t* slots = reinterpret_cast<int32_t*>(at(9));
-    uint16_t* rows = reinterpret_cast<uint16_t*>(at(10));
+    int32_t* rel = reinterpret_cast<int32_t*>(at(10));
     uint16_t* act = reinterpret_cast<uint16_t*>(at(11));
     float* down = reinterpret_cast<float*>(at(12));
     uint32_t* queue = reinterpret_cast<uint32_t*>(at(13));
@@ -620,15 +620,16 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
     const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
-        (e = launch_layout(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu, mtu, nt,
-                           queue, nullptr, nullptr, s)) != hipSuccess ||
-        (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
-                           nt + 1, queue + 2, nullptr, nullptr, s)) != hipSuccess ||
-        (e = launch_gather_bf16(x, M, H, ids, k, E, cursors, sorted, slots, rows, s)) !=
+    // route (clearing the layout's counters); count + sort over many workgroups (sorted route
+    // ids, route -> slot, both task lists); gated-up GEMM gathering its rows from x on load
+    // with the SwiGLU epilogue; down GEMM; combine through the slot table
+    if ((e = launch_route_zero(logits, M, E, k, softcap, ids, wts, counts, rel, E, s)) !=
             hipSuccess ||
-        (e = launch_gemm_bf16(rows, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s)) !=
-            hipSuccess ||
+        (e = launch_layout_sorted_wide(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu,
+                                       nt, queue, rel, sorted, s, slots, nbd, td, nt + 1,
+                                       queue + 2)) != hipSuccess ||
+        (e = launch_gemm_bf16(x, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s,
+                              sorted, k)) != hipSuccess ||
         (e = launch_gemm_bf16(act, F, w_down, H, td, nt + 1, mtd, MOE_EPI_STORE_F32, down, s)) !=
             hipSuccess ||
         (e = launch_scatter(down, slots, wts, ids, M, k, E, H, out, s)) != hipSuccess)

@@ -19,7 +19,9 @@
 // are read during the previous step's MFMAs.  The operand reads are inline ds_read_b128 with
 // explicit lgkmcnt waits tied to the fragment registers: the compiler cannot tell a DMA into
 // one stage from reads of the other and would otherwise drain the DMA before every read.
-// Rows past rc repeat row rb + rc - 1 (never stored).
+// Rows past rc repeat row rb + rc - 1 (never stored).  With a sorted route list the A rows
+// are gathered on load: sorted row s is token row sorted[s] / k of the layer input, so no
+// expert-sorted copy of the input is written first.
 //
 // Order.  Workgroups go round-robin over the 8 XCDs; each XCD takes one contiguous run of the
 // chunk-major task list, regrouped so that the tiles it runs together cover a few chunks x a
@@ -80,7 +82,8 @@ template <int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
                       const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
-                      void* __restrict__ out, int K, int N, int pw, int gch) {
+                      void* __restrict__ out, int K, int N, int pw, int gch,
+                      const int32_t* __restrict__ sorted, int kr) {
     __shared__ uint4 sA[2][kBM * 8];             // 2 stages x 256 rows x 128 bytes
     __shared__ uint4 sW[2][kBN * 8];
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so workgroup b
@@ -124,7 +127,10 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     for (int i = 0; i < 8; ++i) {
         const int r = wave * 64 + i * 8 + dl;   // tile row moved by this lane
         const int dc = (lane & 7) ^ ((r >> 1) & 7);   // global 16-byte chunk this lane moves
-        srcA[i] = a + (size_t)(rb + min(r, rc - 1)) * K + dc * 8;
+        // sorted row rb + r, or with a sorted route list the token row it was routed from
+        const int sr = rb + min(r, rc - 1);
+        const int arow = sorted ? sorted[sr] / kr : sr;
+        srcA[i] = a + (size_t)arow * K + dc * 8;
         int wr;
         if (EPI == MOE_EPI_SWIGLU_BF16)
             wr = r < 128 ? nb * 128 + r : N / 2 + nb * 128 + (r - 128);
@@ -301,7 +307,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
 
 hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
-                            int epilogue, void* out, hipStream_t s) {
+                            int epilogue, void* out, hipStream_t s, const int32_t* sorted,
+                            int kr) {
     if (max_tasks <= 0) return hipSuccess;
     const int4* t = reinterpret_cast<const int4*>(tasks);
     const int grid = (max_tasks + 7) / 8 * 8;    // whole rounds of the 8 XCDs
@@ -311,15 +318,18 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_BF16>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch,
+                               sorted, kr);
             break;
         case MOE_EPI_SWIGLU_BF16:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_SWIGLU_BF16>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch,
+                               sorted, kr);
             break;
         default:
             hipLaunchKernelGGL(gemm_bf16_kernel<MOE_EPI_STORE_F32>, dim3(grid),
-                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch);
+                               dim3(kThreads), 0, s, a, w, t, ntasks, out, K, N, pw, gch,
+                               sorted, kr);
     }
     return hipGetLastError();
 }

@@ -262,7 +262,8 @@ __global__ __launch_bounds__(kThreads) void sort_layout_kernel(
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ cursors, moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks,
     uint32_t* __restrict__ queue, int32_t* __restrict__ rel,
-    int32_t* __restrict__ sorted_route_ids) {
+    int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots, int n_blocks2,
+    moe_task* __restrict__ tasks2, int32_t* __restrict__ ntasks2, uint32_t* __restrict__ queue2) {
     __shared__ int s_h[kThreads];
     __shared__ int s_base[kThreads];
     __shared__ int s_hist[kThreads];
@@ -277,12 +278,21 @@ __global__ __launch_bounds__(kThreads) void sort_layout_kernel(
     const int rank = (unsigned)e < (unsigned)E ? atomicAdd(&s_h[e], 1) : -1;
     int total_rows;
     const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0) {
         write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
                     s_wsum);
+        if (tasks2) {                             // a second list over the same chunks
+            __syncthreads();
+            s_hist[tid] = 0;
+            __syncthreads();
+            write_tasks(c, row0, E, n_blocks2, chunk, offsets, cursors, tasks2, ntasks2, queue2,
+                        s_hist, s_wsum);
+        }
+    }
     if (tid < E && s_h[tid] > 0) s_base[tid] = row0 + atomicAdd(&rel[tid], s_h[tid]);
     __syncthreads();
     if (rank >= 0) sorted_route_ids[s_base[e] + rank] = r;
+    if (route_slots && r < R) route_slots[r] = rank >= 0 ? s_base[e] + rank : -1;
 }
 
 }  // namespace
@@ -312,7 +322,8 @@ hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, in
                                      int chunk_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* cursors, moe_task* tasks, int32_t* ntasks,
                                      uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
-                                     hipStream_t s) {
+                                     hipStream_t s, int32_t* route_slots, int n_blocks2,
+                                     moe_task* tasks2, int32_t* ntasks2, uint32_t* queue2) {
     const int R = M * k;
     if (R == 0) return hipSuccess;
     const unsigned grid = (unsigned)((R + kThreads - 1) / kThreads);
@@ -321,7 +332,7 @@ hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, in
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sort_layout_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
                        n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue, rel,
-                       sorted_route_ids);
+                       sorted_route_ids, route_slots, n_blocks2, tasks2, ntasks2, queue2);
     return hipGetLastError();
 }
 

@@ -17,6 +17,10 @@ const DeviceInfo& device_info();
 
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
                         int32_t* ids, float* weights, hipStream_t s);
+// the same, with zero0[0..zero_n) and zero1[0..zero_n) cleared by its first workgroup
+hipError_t launch_route_zero(const float* logits, int M, int E, int k, float softcap,
+                             int32_t* ids, float* weights, int32_t* zero0, int32_t* zero1,
+                             int zero_n, hipStream_t s);
 
 // route + per-token quantisation of x (token-major codes [M][K], scales [K/128][M])
 hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
@@ -29,12 +33,15 @@ hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, in
                                       uint8_t* x_q, float* x_scales, int32_t* zero0,
                                       int32_t* zero1, int zero_n, hipStream_t s);
 
-// the layout with the sorted route ids over many workgroups: counts and rel [E] must be zero
+// the layout with the sorted route ids over many workgroups: counts and rel [E] must be zero;
+// optionally route -> slot and a second task list over the same chunks (n_blocks2 panels)
 hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, int n_blocks,
                                      int chunk_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* cursors, moe_task* tasks, int32_t* ntasks,
                                      uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
-                                     hipStream_t s);
+                                     hipStream_t s, int32_t* route_slots = nullptr,
+                                     int n_blocks2 = 0, moe_task* tasks2 = nullptr,
+                                     int32_t* ntasks2 = nullptr, uint32_t* queue2 = nullptr);
 
 // sorted_route_ids / route_slots may be null (then the routes are not sorted)
 hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, int chunk_rows,
@@ -101,9 +108,11 @@ hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* count
                          int32_t* offsets, hipStream_t s);
 
 // BF16 grouped GEMM (256 x 256 tiles; STORE_F32, STORE_BF16, SWIGLU_BF16)
+// (with sorted != nullptr, A row s is row sorted[s] / kr of a: gathered on load)
 hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
-                            int epilogue, void* out, hipStream_t s);
+                            int epilogue, void* out, hipStream_t s,
+                            const int32_t* sorted = nullptr, int kr = 1);
 
 // silu(g) * u requantised per 128 columns (the FP8 expert MLP's activation step)
 hipError_t launch_swiglu_quant(const float* h, int R, int I, uint8_t* a_q, float* a_scales,

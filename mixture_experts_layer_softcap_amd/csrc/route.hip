@@ -189,6 +189,13 @@ hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
                             nullptr, nullptr, nullptr, 0, s);
 }
 
+hipError_t launch_route_zero(const float* logits, int M, int E, int k, float softcap,
+                             int32_t* ids, float* weights, int32_t* zero0, int32_t* zero1,
+                             int zero_n, hipStream_t s) {
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, nullptr, 0, nullptr,
+                            nullptr, zero0, zero1, zero_n, s);
+}
+
 hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
                                  int K, float softcap, int32_t* ids, float* weights,
                                  uint8_t* x_q, float* x_scales, hipStream_t s) {

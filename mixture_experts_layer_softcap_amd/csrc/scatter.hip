@@ -15,15 +15,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// The k routes of a token are read in groups of kGroup: every load of a group (ids, weights,
-// slots, rows) is issued before any is used, so a group costs one round trip (two with a slot
-// table), whatever the ids hold; indices past k or behind an invalid id are clamped and their
-// terms skipped.
-constexpr int kGroup = 8;
-
+// The k routes of a token are read in groups of G (2, 4 or 8, the smallest that holds k, else
+// 8): every load of a group (ids, weights, slots, rows) is issued before any is used, so a
+// group costs one round trip (two with a slot table), whatever the ids hold; indices past k or
+// behind an invalid id are clamped and their terms skipped.
+//
 // CPT output columns per thread (4, 2 or 1): small batches use narrower threads so the grid
 // covers every CU (a CU's requests in flight, not the bytes, bound this kernel).
-template <bool SLOTS, int CPT>
+template <bool SLOTS, int CPT, int kGroup>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const float* __restrict__ rows, const int32_t* __restrict__ route_slots,
     const float* __restrict__ weights, const int32_t* __restrict__ ids, int M, int k, int E,
@@ -70,6 +69,22 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     }
 }
 
+template <bool SLOTS, int CPT>
+hipError_t launch_cpt(const float* rows, const int32_t* route_slots, const float* weights,
+                      const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
+                      unsigned grid, hipStream_t s) {
+    if (k <= 2)
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 2>), dim3(grid), dim3(kThreads), 0, s,
+                           rows, route_slots, weights, ids, M, k, E, N, out);
+    else if (k <= 4)
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 4>), dim3(grid), dim3(kThreads), 0, s,
+                           rows, route_slots, weights, ids, M, k, E, N, out);
+    else
+        hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 8>), dim3(grid), dim3(kThreads), 0, s,
+                           rows, route_slots, weights, ids, M, k, E, N, out);
+    return hipGetLastError();
+}
+
 template <bool SLOTS>
 hipError_t launch_slots(const float* rows, const int32_t* route_slots, const float* weights,
                         const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
@@ -81,15 +96,10 @@ hipError_t launch_slots(const float* rows, const int32_t* route_slots, const flo
     const size_t work = (size_t)M * (N / cpt);
     const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
     if (cpt == 4)
-        hipLaunchKernelGGL((scatter_kernel<SLOTS, 4>), dim3(grid), dim3(kThreads), 0, s, rows,
-                           route_slots, weights, ids, M, k, E, N, out);
-    else if (cpt == 2)
-        hipLaunchKernelGGL((scatter_kernel<SLOTS, 2>), dim3(grid), dim3(kThreads), 0, s, rows,
-                           route_slots, weights, ids, M, k, E, N, out);
-    else
-        hipLaunchKernelGGL((scatter_kernel<SLOTS, 1>), dim3(grid), dim3(kThreads), 0, s, rows,
-                           route_slots, weights, ids, M, k, E, N, out);
-    return hipGetLastError();
+        return launch_cpt<SLOTS, 4>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
+    if (cpt == 2)
+        return launch_cpt<SLOTS, 2>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
+    return launch_cpt<SLOTS, 1>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
 }
 
 }  // namespace
