@@ -277,27 +277,37 @@ def bench_mlp(args, moe, synth, torch, np):
     per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
     us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
 
-    # the gate+up GEMM alone on the sorted FP8 rows, tasks and ids the last step left
     def wsp(i, dtype, n):
         o = moe.mlp_workspace_offset(M, E, k, H, I, i)
         return ws[o:o + n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if H <= 8192 else 64))
-    mtu = moe.max_tasks(M, k, E, 2 * I // 128, chunk)
-    a_q = wsp(10, torch.uint8, R * H).view(R, H)
-    a_s = wsp(11, torch.float32, (H // 128) * R)
-    tasks = wsp(5, torch.int32, 4 * mtu).view(mtu, 4)
-    nt = wsp(7, torch.int32, 1)
-    o7 = moe.mlp_workspace_offset(M, E, k, H, I, 7)
-    queue = ws[o7 + 16:o7 + 24].view(torch.int32)
-    sorted_ids = wsp(8, torch.int32, R)
+    fused = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows) == 6
     h1 = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
+    if fused:
+        # the gate+up GEMM alone, straight from the routed ids the last step left (part 0)
+        ids_ws = wsp(0, torch.int32, R).view(M, k)
 
-    def gemm(i):
-        a = w1s[i % copies]
-        moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, a[0], a[1], tasks, nt, chunk, h1,
-                         moe.MOE_EPI_STORE_F32, queue=queue, sorted_route_ids=sorted_ids)
+        def gemm(i):
+            a = w1s[i % copies]
+            moe.grouped_gemm_routed(x, ids_ws, E, a[0], a[1], h1)
+    else:
+        # the gate+up GEMM alone on the sorted FP8 rows, tasks and ids the last step left
+        mtu = moe.max_tasks(M, k, E, 2 * I // 128, chunk)
+        a_q = wsp(10, torch.uint8, R * H).view(R, H)
+        a_s = wsp(11, torch.float32, (H // 128) * R)
+        tasks = wsp(5, torch.int32, 4 * mtu).view(mtu, 4)
+        nt = wsp(7, torch.int32, 1)
+        o7 = moe.mlp_workspace_offset(M, E, k, H, I, 7)
+        queue = ws[o7 + 16:o7 + 24].view(torch.int32)
+        sorted_ids = wsp(8, torch.int32, R)
+
+        def gemm(i):
+            a = w1s[i % copies]
+            moe.grouped_gemm(moe.MOE_GEMM_FP8_B128, a_q, a_s, a[0], a[1], tasks, nt, chunk,
+                             h1, moe.MOE_EPI_STORE_F32, queue=queue,
+                             sorted_route_ids=sorted_ids)
 
     for i in range(2 * copies):
         gemm(i)
@@ -314,13 +324,15 @@ def bench_mlp(args, moe, synth, torch, np):
     counts = np.bincount(ids_np, minlength=E)
     nonempty = int((counts > 0).sum())
     N1 = 2 * I
-    gbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4) + R * H + (H // 128) * R * 4 \
-        + R * 4 + R * N1 * 4
+    acts = (M * H * 2 + R * 4) if fused else (R * H + (H // 128) * R * 4 + R * 4)
+    gbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4) + acts + R * N1 * 4
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
     lbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4) \
         + M * E * 4 + M * H * 2 + M * H * 2
     flops = 2.0 * R * (N1 * H + H * I)
-    gemm_kernel = ("gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
+    gemm_kernel = ("gemm_fp8_fused_kernel (gate+up grouped FP8 GEMM from routed ids, rows at "
+                   "route ids)" if fused else
+                   "gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
                    if H == 2048 and chunk <= 16 else
                    "gemm_fp8_tile_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
                    if 64 < chunk <= 256 and H <= 8192 else
@@ -333,8 +345,11 @@ def bench_mlp(args, moe, synth, torch, np):
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "H": H, "I": I,
                    "softcap": cap, "weight_copies_rotated": copies, "chunk_rows": chunk,
-                   "path": "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "
-                           "silu*up requantise, down GEMM, combine"},
+                   "path": ("6 kernels: route, layout (down tasks, sorted ids), gate+up GEMM "
+                            "from the routed ids, silu*up requantise, down GEMM gathering by "
+                            "sorted id, combine" if fused else
+                            "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "
+                            "silu*up requantise, down GEMM, combine")},
         "effective_tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
         "layer_hbm_frac": round(lbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -658,6 +658,20 @@ int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which) {
     return (int64_t)mlp_layout(M, E, k, H, I).off[which];
 }
 
+int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows) {
+    if (!mlp_dims_ok(M, E, k, H, I)) return MOE_E_INVAL;
+    const int Kmax = H > I ? H : I;
+    if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && Kmax > 8192))
+        return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, H);
+    if (!chunk_rows && chunk > 64 && Kmax > 8192) chunk = 64;
+    return forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)
+               ? 6
+               : 7;
+}
+
 int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
                     const float* w1_scales, const uint8_t* w2_q, const float* w2_scales, int M,
                     int E, int k, int H, int I, float softcap, uint16_t* out, void* workspace,
@@ -700,6 +714,23 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)) {
+        // small batch: the gate+up GEMM straight from the routed ids (layout, gather and
+        // quantisation of x inside) with rows at route ids; the activations stay in route
+        // order and the down GEMM gathers its rows by sorted route id
+        if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
+            (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
+                               nt + 1, queue + 2, sorted, nullptr, s)) != hipSuccess ||
+            (e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s)) !=
+                hipSuccess ||
+            (e = launch_swiglu_quant(h1, R, I, aq, as, s)) != hipSuccess ||
+            (e = launch_gemm_fp8_range(aq, as, R, I, w2_q, w2_scales, H, td, nt + 1, mtd,
+                                       MOE_EPI_ROUTE_F32, sorted, h2, s, sorted)) !=
+                hipSuccess ||
+            (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s)) != hipSuccess)
+            return hip_status(e);
+        return MOE_OK;
+    }
     if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
         (e = launch_layout2(ids, M, k, E, chunk, counts, offsets, cursors, nbu, tu, nt, queue,
                             nbd, td, nt + 1, queue + 2, s)) != hipSuccess ||

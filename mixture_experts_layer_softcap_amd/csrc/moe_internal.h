@@ -75,11 +75,12 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, in
 
 // contiguous-range form for tasks of at most 16 routed rows and K = 2048
 bool gemm_fp8_range_applies(int K, int chunk_rows);
+// (a_rows != nullptr: sorted row s of the operand is row a_rows[s] of a and its scales)
 hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int rows, int K,
                                  const uint8_t* w, const float* w_scales, int N,
                                  const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                                  int epilogue, const int32_t* sorted, void* out,
-                                 hipStream_t s);
+                                 hipStream_t s, const int32_t* a_rows = nullptr);
 
 // tiled form for chunks of 65..256 routed rows (both operands staged in LDS)
 bool gemm_fp8_tile_applies(int K, int chunk_rows);

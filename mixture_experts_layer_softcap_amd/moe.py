@@ -60,6 +60,7 @@ SIGNATURES = {
     "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _P]),
     "moe_swiglu_quant": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "moe_mlp_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I]),
     "moe_mlp_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_mlp_forward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I,
                              _P]),
@@ -272,6 +273,13 @@ def mlp_workspace_bytes(M: int, E: int, k: int, H: int, I: int) -> int:
     v = lib().moe_mlp_workspace_bytes(M, E, k, H, I)
     if v == 0:
         raise MoeError("moe_mlp_workspace_bytes", MOE_E_INVAL)
+    return v
+
+
+def mlp_forward_kernels(M: int, E: int, k: int, H: int, I: int, chunk_rows: int = 0) -> int:
+    v = lib().moe_mlp_forward_kernels(M, E, k, H, I, chunk_rows)
+    if v < 0:
+        raise MoeError("moe_mlp_forward_kernels", v)
     return v
 
 

@@ -142,6 +142,8 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert sq(P, 4, 200, P, P, S) == INVAL                                       # I % 128
     assert sq(P, -1, 256, P, P, S) == INVAL
     assert sq(NULL, 4, 256, P, P, S) == INVAL
+    assert L.moe_mlp_forward_kernels(16, 8, 2, 256, 100, 0) == INVAL            # I % 128
+    assert L.moe_mlp_forward_kernels(16, 8, 2, 256, 128, 300) == INVAL           # chunk
     mw = L.moe_mlp_workspace_bytes(16, 8, 2, 256, 128)
     mf = L.moe_mlp_forward
     assert mf(P, P, P, P, P, P, 16, 8, 2, 256, 128, 30.0, P, P, mw - 1, 0, S) == NOSPC

@@ -141,13 +141,15 @@ def ws_part(ws, d, which, dtype, n):
     return to_np(ws[off:off + size]).view(dtype)
 
 
-@pytest.mark.parametrize("M,E,k,H,I,chunk", [
-    (8, 16, 2, 256, 256, 0),       # the correctness-sized layer; general GEMM for both
-    (37, 5, 3, 384, 384, 64),      # ragged segments, 64-row chunks
-    (64, 8, 2, 2048, 512, 16),     # streaming range GEMM (K = 2048) then the general one
-    (64, 8, 2, 2048, 512, 128),    # LDS-tiled GEMM for both projections
+@pytest.mark.parametrize("M,E,k,H,I,chunk,kernels", [
+    (8, 16, 2, 256, 256, 0, 7),       # the correctness-sized layer; general GEMM for both
+    (37, 5, 3, 384, 384, 64, 7),      # ragged segments, 64-row chunks
+    (64, 8, 2, 2048, 512, 16, 6),     # small batch: gate+up from the routed ids, down GEMM
+                                      # gathering its rows by sorted route id
+    (64, 8, 2, 2048, 512, 128, 7),    # LDS-tiled GEMM for both projections
 ])
-def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk):
+def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
+    assert moe.mlp_forward_kernels(M, E, k, H, I, chunk) == kernels
     d = synth.mlp_inputs(M, E, k, H, I, seed=M + H)
     outs, ws = gpu_mlp(d, chunk=chunk, reps=2)
     _, y64 = orc.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
@@ -166,6 +168,7 @@ def test_mlp_forward_full_size_sampled():
     # expert width 512 (gate+up 1024 columns)
     d = synth.mlp_inputs(**{kk: v for kk, v in
                             synth.MLP_WORKLOADS["mlp_fp8_M128_E256_k8_H2048_I512"].items()})
+    assert moe.mlp_forward_kernels(d["M"], d["E"], d["k"], d["H"], d["I"]) == 6
     outs, _ = gpu_mlp(d, reps=2)
     g = np.random.default_rng(0)
     toks = np.unique(np.concatenate([[0, d["M"] - 1], g.choice(d["M"], 14, replace=False)]))
