@@ -15,10 +15,11 @@
 // chunk c of row r stored at position c ^ ((r/2) % 8), so the DMA reads whole cache lines and
 // the MFMA fragment reads are free of LDS bank conflicts.  Two stages of 64 KiB alternate;
 // one barrier per k step publishes a stage and frees the other.  The next stage's DMA
-// instructions are spread over the current stage's MFMAs, and each 16-wide step's fragments
-// are read during the previous step's MFMAs.  The operand reads are inline ds_read_b128 with
-// explicit lgkmcnt waits tied to the fragment registers: the compiler cannot tell a DMA into
-// one stage from reads of the other and would otherwise drain the DMA before every read.
+// instructions go out between the first half of the current stage's MFMAs, and each 16-wide
+// step's fragments are read during the previous step's MFMAs.  The operand reads are inline
+// ds_read_b128 with explicit lgkmcnt waits tied to the fragment registers: the compiler
+// cannot tell a DMA into one stage from reads of the other and would otherwise drain the DMA
+// before every read.
 // Rows past rc repeat row rb + rc - 1 (never stored).  With a sorted route list the A rows
 // are gathered on load: sorted row s is token row sorted[s] / k of the layer input, so no
 // expert-sorted copy of the input is written first.
@@ -197,10 +198,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     };
 
     // One k step from buffer boff: the fragments of 16-wide step st+1 are read while the
-    // MFMAs of step st run.  With DMA, the next k step's 16 DMA instructions are spread over
-    // the step's 64 MFMAs (one after every fourth): a wave issues in order, and a burst of DMA
-    // instructions stalls it on the memory pipeline long enough to hold back its MFMAs, so
-    // the two would otherwise run one after the other.
+    // MFMAs of step st run.  With DMA, the next k step's 16 DMA instructions go out one after
+    // every second MFMA of the step's first half: a wave issues in order, and a burst of DMA
+    // instructions stalls it on the memory pipeline long enough to hold back its MFMAs, while
+    // DMA issued late in the step leaves its latency to the next barrier (one per fourth MFMA
+    // over the whole step measured 3-7 % slower).
     auto compute = [&](uint32_t boff, int nbuf, int nkt, auto with_dma) {
         uint4* dA = sA[nbuf];
         uint4* dW = sW[nbuf];
@@ -223,20 +225,25 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < 4; ++ni) {
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[ni], A[mi],
                                                                          acc[mi][ni], 0, 0, 0);
-                if constexpr (decltype(with_dma)::value) {
-                    const int i = 2 * st + (mi >> 1);          // DMA row group of this wave
-                    const int row0 = wave * 64 + i * 8;
-                    if (mi & 1)
-                        __builtin_amdgcn_global_load_lds(srcW[i] + k0,
-                                                         (lds_void*)(dW + row0 * 8), 16, 0, 0);
-                    else
-                        __builtin_amdgcn_global_load_lds(srcA[i] + k0,
-                                                         (lds_void*)(dA + row0 * 8), 16, 0, 0);
+                    if constexpr (decltype(with_dma)::value) {
+                        const int m = st * 16 + mi * 4 + ni;     // MFMA index in the step
+                        if (m % 2 == 1 && m / 2 < 16) {
+                            const int q = m / 2;                     // DMA index 0..15
+                            const int i = q >> 1;
+                            const int row0 = wave * 64 + i * 8;
+                            if (q & 1)
+                                __builtin_amdgcn_global_load_lds(srcW[i] + k0,
+                                    (lds_void*)(dW + row0 * 8), 16, 0, 0);
+                            else
+                                __builtin_amdgcn_global_load_lds(srcA[i] + k0,
+                                    (lds_void*)(dA + row0 * 8), 16, 0, 0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
