@@ -199,10 +199,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
 
     // One k step from buffer boff: the fragments of 16-wide step st+1 are read while the
     // MFMAs of step st run.  With DMA, the next k step's 16 DMA instructions go out one after
-    // every second MFMA of the step's first half: a wave issues in order, and a burst of DMA
-    // instructions stalls it on the memory pipeline long enough to hold back its MFMAs, while
-    // DMA issued late in the step leaves its latency to the next barrier (one per fourth MFMA
-    // over the whole step measured 3-7 % slower).
+    // every second MFMA of the step's first half, from the first on: a wave issues in order,
+    // and a burst of DMA instructions stalls it on the memory pipeline long enough to hold
+    // back its MFMAs, while DMA issued late in the step leaves its latency to the next
+    // barrier (one per fourth MFMA over the whole step measured 3-7 % slower, one per third
+    // 1-3 % slower).
     auto compute = [&](uint32_t boff, int nbuf, int nkt, auto with_dma) {
         uint4* dA = sA[nbuf];
         uint4* dW = sW[nbuf];
@@ -230,7 +231,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
                                                                          acc[mi][ni], 0, 0, 0);
                     if constexpr (decltype(with_dma)::value) {
                         const int m = st * 16 + mi * 4 + ni;     // MFMA index in the step
-                        if (m % 2 == 1 && m / 2 < 16) {
+                        if (m % 2 == 0 && m / 2 < 16) {
                             const int q = m / 2;                     // DMA index 0..15
                             const int i = q >> 1;
                             const int row0 = wave * 64 + i * 8;
