@@ -13,9 +13,10 @@
 // Operands.  Both tiles go from global memory straight into LDS with global_load_lds_dwordx4:
 // one instruction moves 8 whole 128-byte row segments (64 k values of 8 rows), each 16-byte
 // chunk c of row r stored at position c ^ ((r/2) % 8), so the DMA reads whole cache lines and
-// the MFMA fragment reads are free of LDS bank conflicts.  Two stages of 64 KiB alternate;
-// one barrier per k step publishes a stage and frees the other.  The next stage's DMA
-// instructions go out between the first half of the current stage's MFMAs, and each 16-wide
+// the MFMA fragment reads are free of LDS bank conflicts.  The routed rows have two stages
+// of 32 KiB and the weights three (all 160 KiB of LDS): the weight DMA runs two k steps
+// ahead, the row DMA one; one barrier per k step publishes a stage and frees the oldest.  The
+// DMA instructions go out between the first half of the current stage's MFMAs, and each 16-wide
 // step's fragments are read during the previous step's MFMAs.  The operand reads are inline
 // ds_read_b128 with explicit lgkmcnt waits tied to the fragment registers: the compiler
 // cannot tell a DMA into one stage from reads of the other and would otherwise drain the DMA
@@ -85,8 +86,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
                       const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                       void* __restrict__ out, int K, int N, int pw, int gch,
                       const int32_t* __restrict__ sorted, int kr) {
-    __shared__ uint4 sA[2][kBM * 8];             // 2 stages x 256 rows x 128 bytes
-    __shared__ uint4 sW[2][kBN * 8];
+    __shared__ uint4 sA[2][kBM * 8];             // routed rows: 2 stages x 256 x 128 bytes
+    __shared__ uint4 sW[3][kBN * 8];             // weights: three stages
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so workgroup b
     // runs on XCD b%8; each XCD takes one contiguous run of the (chunk-major) task list, so
     // the tiles running together on an XCD share routed-row chunks and weight panels, and
@@ -140,17 +141,6 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
         srcW[i] = w + ((size_t)e * N + wr) * K + dc * 8;
     }
 
-    auto issue = [&](int buf, int kt) {
-        uint4* dA = sA[buf];
-        uint4* dW = sW[buf];
-        const int k0 = kt * kBK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row0 = wave * 64 + i * 8;
-            __builtin_amdgcn_global_load_lds(srcA[i] + k0, (lds_void*)(dA + row0 * 8), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(srcW[i] + k0, (lds_void*)(dW + row0 * 8), 16, 0, 0);
-        }
-    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -185,8 +175,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     struct Frag {
         i32x4 a0, a1, a2, a3, w0, w1, w2, w3;
     };
-    auto read_frags = [&](Frag& f, uint32_t boff, int st) __attribute__((always_inline)) {
-        const uint32_t qa = pa[st] + boff, qw0 = pw0[st] + boff, qw2 = pw2[st] + boff;
+    auto read_frags = [&](Frag& f, uint32_t boffA, uint32_t boffW, int st)
+                          __attribute__((always_inline)) {
+        const uint32_t qa = pa[st] + boffA, qw0 = pw0[st] + boffW, qw2 = pw2[st] + boffW;
         f.a0 = lds_read16<0 * 4096>(qa);
         f.a1 = lds_read16<1 * 4096>(qa);
         f.a2 = lds_read16<2 * 4096>(qa);
@@ -204,17 +195,18 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     // back its MFMAs, while DMA issued late in the step leaves its latency to the next
     // barrier (one per fourth MFMA over the whole step measured 3-7 % slower, one per third
     // 1-3 % slower).
-    auto compute = [&](uint32_t boff, int nbuf, int nkt, auto with_dma) {
-        uint4* dA = sA[nbuf];
-        uint4* dW = sW[nbuf];
-        const int k0 = nkt * kBK;
+    auto compute = [&](uint32_t boffA, uint32_t boffW, int nbufA, int nbufW, int nktA,
+                       int nktW, auto dma_a, auto dma_w) {
+        uint4* dA = sA[nbufA];
+        uint4* dW = sW[nbufW];
+        const int k0A = nktA * kBK, k0W = nktW * kBK;
         Frag f[2];
-        read_frags(f[0], boff, 0);
+        read_frags(f[0], boffA, boffW, 0);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             Frag& c = f[st & 1];
             if (st < 3) {
-                read_frags(f[(st + 1) & 1], boff, st + 1);
+                read_frags(f[(st + 1) & 1], boffA, boffW, st + 1);
                 lds_wait<8>(c.a0, c.a1, c.a2, c.a3, c.w0, c.w1, c.w2, c.w3);
             } else {
                 lds_wait<0>(c.a0, c.a1, c.a2, c.a3, c.w0, c.w1, c.w2, c.w3);
@@ -229,18 +221,22 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
                 for (int ni = 0; ni < 4; ++ni) {
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B[ni], A[mi],
                                                                          acc[mi][ni], 0, 0, 0);
-                    if constexpr (decltype(with_dma)::value) {
+                    {
                         const int m = st * 16 + mi * 4 + ni;     // MFMA index in the step
                         if (m % 2 == 0 && m / 2 < 16) {
-                            const int q = m / 2;                     // DMA index 0..15
-                            const int i = q >> 1;
-                            const int row0 = wave * 64 + i * 8;
-                            if (q & 1)
-                                __builtin_amdgcn_global_load_lds(srcW[i] + k0,
-                                    (lds_void*)(dW + row0 * 8), 16, 0, 0);
-                            else
-                                __builtin_amdgcn_global_load_lds(srcA[i] + k0,
-                                    (lds_void*)(dA + row0 * 8), 16, 0, 0);
+                            const int q = m / 2;                     // DMA slot 0..15
+                            if (q < 8) {
+                                if constexpr (decltype(dma_a)::value)
+                                    __builtin_amdgcn_global_load_lds(
+                                        srcA[q] + k0A, (lds_void*)(dA + (wave * 64 + q * 8) * 8),
+                                        16, 0, 0);
+                            } else {
+                                if constexpr (decltype(dma_w)::value)
+                                    __builtin_amdgcn_global_load_lds(
+                                        srcW[q - 8] + k0W,
+                                        (lds_void*)(dW + (wave * 64 + (q - 8) * 8) * 8), 16, 0,
+                                        0);
+                            }
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -249,15 +245,41 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
         }
     };
 
-    // k step kt on buffer kt%2: wait for it (the DMA of step kt+1 is not issued yet), publish
-    // it and free the other buffer, compute while the DMA of step kt+1 fills that buffer
-    issue(0, 0);
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        barrier_after_vmcnt<0>();
-        compute((kt & 1) ? kStage : 0u, (kt + 1) & 1, kt + 1, std::integral_constant<bool, true>{});
+    // Weights run two steps ahead (three stages), routed rows one (two stages).  Step kt
+    // issues A(kt+1), then W(kt+2); its barrier waits for A(kt) and W(kt), leaving W(kt+1)
+    // (the newest 8 DMA instructions) in flight.
+    auto issueA = [&](int buf, int kt) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(srcA[i] + k0,
+                                             (lds_void*)(sA[buf] + (wave * 64 + i * 8) * 8), 16,
+                                             0, 0);
+    };
+    auto issueW = [&](int buf, int kt) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(srcW[i] + k0,
+                                             (lds_void*)(sW[buf] + (wave * 64 + i * 8) * 8), 16,
+                                             0, 0);
+    };
+    using T = std::integral_constant<bool, true>;
+    issueA(0, 0);
+    issueW(0, 0);
+    issueW(1, min(1, nk - 1));
+    int bw = 0;                                 // kt % 3
+    for (int kt = 0; kt < nk; ++kt) {
+        // A(kt) and W(kt) have landed; W(kt+1) (the newest 8) may still be in flight.  Past
+        // the end the DMA repeats the last stage into a free buffer (never read).
+        barrier_after_vmcnt<8>();
+        const uint32_t bA = (kt & 1) ? kStage : 0u, bW = (uint32_t)bw * kStage;
+        const int bw2 = bw == 0 ? 2 : bw - 1;   // (kt + 2) % 3
+        compute(bA, bW, (kt + 1) & 1, bw2, min(kt + 1, nk - 1), min(kt + 2, nk - 1), T{}, T{});
+        bw = bw == 2 ? 0 : bw + 1;
     }
+    // no DMA may still write this workgroup's LDS when it exits
     barrier_after_vmcnt<0>();
-    compute(((nk - 1) & 1) ? kStage : 0u, 0, 0, std::integral_constant<bool, false>{});
 
     // C layout of the 32x32 MFMA: lane (j, h) holds column j (routed row) and, in register
     // r, output row 8*(r/4) + 4*h + r%4 of the 32-row weight group
