@@ -125,14 +125,23 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict
     const int dl = lane >> 3;                   // row within a DMA instruction
     const uint16_t* srcA[8];
     const uint16_t* srcW[8];
+    // A row of tile row r: sorted row rb + r, or with a sorted route list the token row it was
+    // routed from (the eight lookups issued together)
+    int arow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) arow[i] = rb + min(wave * 64 + i * 8 + dl, rc - 1);
+    if (sorted) {
+        int v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = sorted[arow[i]];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) arow[i] = v[i] / kr;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = wave * 64 + i * 8 + dl;   // tile row moved by this lane
         const int dc = (lane & 7) ^ ((r >> 1) & 7);   // global 16-byte chunk this lane moves
-        // sorted row rb + r, or with a sorted route list the token row it was routed from
-        const int sr = rb + min(r, rc - 1);
-        const int arow = sorted ? sorted[sr] / kr : sr;
-        srcA[i] = a + (size_t)arow * K + dc * 8;
+        srcA[i] = a + (size_t)arow[i] * K + dc * 8;
         int wr;
         if (EPI == MOE_EPI_SWIGLU_BF16)
             wr = r < 128 ? nb * 128 + r : N / 2 + nb * 128 + (r - 128);
