@@ -351,8 +351,9 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
     if (max_tasks <= 0) return hipSuccess;
     const int4* t = reinterpret_cast<const int4*>(tasks);
     const int grid = (max_tasks + 7) / 8 * 8;    // whole rounds of the 8 XCDs
-    // tile groups of ~32 (one XCD's CUs): up to 8 panels x 32/8 chunks
-    const int pw = min(8, N / kBN);
+    // tile groups of ~32 (one XCD's CUs): up to 4 panels x 32/4 chunks (8 x 4 and 12 x 2 were
+    // 1-4 % slower with three weight stages)
+    const int pw = min(4, N / kBN);
     const int gch = 32 / pw;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
