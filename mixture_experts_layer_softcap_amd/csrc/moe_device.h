@@ -56,12 +56,14 @@ __device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, floa
 }
 
 // Router selection key of logit v of expert e: the high word orders the float (-0 ranks equal
-// to +0), the low word holds 0xFFFFFFFF - e so equal logits resolve to the lower expert index.
-// Keys of one token's experts are distinct; its top-k are the k largest keys.
+// to +0; a NaN ranks below every number, -inf included, and NaNs tie with each other), the low
+// word holds 0xFFFFFFFF - e so equal logits resolve to the lower expert index.  Keys of one
+// token's experts are distinct; its top-k are the k largest keys.
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
     uint32_t u = __float_as_uint(v);
     if (u == 0x80000000u) u = 0u;
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) ord = 0u;    // NaN: below -inf (0x007FFFFF)
     return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 

@@ -97,12 +97,15 @@ int orc_route(const float* logits, int M, int E, int k, float cap, int32_t* ids,
         memset(taken, 0, (size_t)E);
         /* Selection by the raw logit: softcap and softmax are strictly increasing maps, so
          * the top-k of the probabilities is the top-k of the logits.  Repeated argmax with
-         * a strict comparison keeps the lowest index among equal values (and -0 == +0). */
+         * a strict comparison keeps the lowest index among equal values (and -0 == +0).
+         * The pages say nothing of non-finite logits; a NaN is taken to rank below every
+         * number, so it is chosen only when fewer than k numbers remain, lowest index first. */
         for (int j = 0; j < k; ++j) {
             int best = -1;
             for (int e = 0; e < E; ++e) {
                 if (taken[e]) continue;
-                if (best < 0 || row[e] > row[best]) best = e;
+                if (best < 0 || (!isnan(row[e]) && (isnan(row[best]) || row[e] > row[best])))
+                    best = e;
             }
             taken[best] = 1;
             ids[(size_t)t * k + j] = best;

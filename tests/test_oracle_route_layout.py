@@ -44,6 +44,30 @@ def test_route_negative_zero_equals_positive_zero(orc):
     assert w[0].tolist() == [0.5, 0.5]
 
 
+def test_route_nan_ranks_below_every_number(orc):
+    # reading of the pages (silent on non-finite logits): a NaN ranks below -inf and NaNs tie,
+    # so they are chosen last, lowest index first.  Brute force: a stable sort on the key
+    # (is NaN, -value), with NaN values replaced by 0 so that only the flag orders them.
+    g = np.random.default_rng(11)
+    logits = g.standard_normal((6, 16)).astype(np.float32)
+    logits[0, [2, 9]] = np.nan
+    logits[1, :] = np.nan
+    logits[2, 3] = -np.inf
+    logits[2, [0, 5, 6]] = np.nan
+    logits[3, ::2] = np.nan
+    logits[4, 1:] = np.nan
+    logits[5, 7] = np.inf
+    logits[5, 8] = np.nan
+    for k in (1, 4, 9, 16):
+        ids, _ = orc.route(logits, k, 30.0)
+        nan = np.isnan(logits)
+        key = np.where(nan, 0.0, -(logits.astype(np.float64) + 0.0))
+        ref = np.lexsort((key, nan), axis=1)[:, :k]   # primary: NaN flag, then -value
+        np.testing.assert_array_equal(ids, ref)
+    ids, _ = orc.route(logits, 2, 30.0)
+    assert ids[1].tolist() == [0, 1] and ids[2, 0] != 3 and ids[4].tolist() == [0, 1]
+
+
 @pytest.mark.parametrize("k", [1, 2, 8])
 def test_route_all_equal_logits_give_exact_uniform_weights(orc, k):
     logits = np.full((3, 16), 0.75, np.float32)
