@@ -2,7 +2,9 @@
 segment canonicalisation, cached full-size workloads."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import functools
+import os
 
 import numpy as np
 import torch
@@ -17,9 +19,12 @@ REL_FRO = 5e-3
 ELEM_RMS = 2e-2
 WEIGHT_RTOL = 1e-5
 # fp32 rows of the FP8 grouped GEMM against the exact (double) oracle.  The matrix core sums
-# the 128 products of one scale block at reduced precision (about 2^-13 of the block's
-# magnitude was measured); the kernel promotes every block to fp32, so the error stays one
-# block's rounding per block.
+# the 128 products of one scale block at reduced precision: test_fp8_block_sum_error_of_the_
+# matrix_core measures at most 2^-12.1 (median 2^-14 to 2^-16) of the block's absolute sum
+# T = sum |a_i w_i| on random E4M3 codes and holds it to 2^-11; products of like magnitude
+# are summed exactly.  The kernel promotes every block to fp32, so a row carries one such
+# error per block; with T about sqrt(128) times the block sum's rms on random data, 16
+# blocks give about 1e-4 of the row's rms, which these bounds allow.
 GEMM_F32_REL_FRO = 1e-4
 GEMM_F32_ELEM_RMS = 5e-4
 
@@ -48,15 +53,32 @@ def bf16_f64(bits: np.ndarray) -> np.ndarray:
     return synth.bf16_to_f32(np.asarray(bits).view(np.uint16)).astype(np.float64)
 
 
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of the bf16 values at |v| (8 significant bits; normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
 def assert_bf16_close(y_bits: np.ndarray, ref64: np.ndarray, what: str = ""):
+    """The BF16 output bar: relative Frobenius error <= REL_FRO and, per element, |d| <=
+    ELEM_RMS * rms(ref).  A bf16 output cannot be closer to the exact value than half a bf16
+    ulp, which exceeds ELEM_RMS * rms wherever |ref| > 2^8 * ELEM_RMS * rms (5.1 rms), so
+    there the per-element bound is one bf16 ulp of the reference (the rounding of an fp32
+    value a little off the exact one)."""
     y = bf16_f64(y_bits)
     ref = np.asarray(ref64, np.float64)
     assert np.isfinite(y).all(), f"{what}: non-finite output"
     rms = float(np.sqrt(np.mean(ref ** 2)))
     fro = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
-    worst = float(np.abs(y - ref).max()) if y.size else 0.0
     assert fro <= REL_FRO, f"{what}: relative Frobenius error {fro:.3e} > {REL_FRO}"
-    assert worst <= ELEM_RMS * rms, f"{what}: max |d| {worst:.3e} > {ELEM_RMS}*rms ({rms:.3e})"
+    if not y.size:
+        return
+    d = np.abs(y - ref)
+    bound = np.maximum(ELEM_RMS * rms, bf16_ulp(ref))
+    i = int(np.argmax(d - bound))
+    assert d.flat[i] <= bound.flat[i], (
+        f"{what}: |d| {d.flat[i]:.3e} at ref {ref.flat[i]:.4g} > max({ELEM_RMS}*rms "
+        f"({ELEM_RMS * rms:.3e}), bf16 ulp)")
 
 
 def assert_gemm_f32_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
@@ -86,3 +108,41 @@ def workload(name: str):
     w_q, w_s = oracle.quant_weights(d["w"])
     d["w_q"], d["w_s"] = w_q, w_s
     return d
+
+
+def oracle_threads() -> int:
+    # the box gives one GPU a share of 16 host cores, whatever os.cpu_count() says
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_rows_parallel(fn, items: np.ndarray, *args, parts: int = 0):
+    """Run a single-threaded oracle routine fn(*args, items_part) on parts of `items` (token
+    or row lists) in threads and stack the results.  The oracle's C routines release the GIL
+    while they run (ctypes), so the parts run on separate host cores; each part is the plain
+    serial computation of its own tokens or rows."""
+    items = np.ascontiguousarray(items, np.int32)
+    n = parts or oracle_threads()
+    chunks = [c for c in np.array_split(items, n) if c.size]
+    with cf.ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+        res = list(ex.map(lambda c: fn(*args, c), chunks))
+    if isinstance(res[0], tuple):
+        return tuple(np.concatenate([r[i] for r in res]) for i in range(len(res[0])))
+    return np.concatenate(res)
+
+
+def oracle_gemm_rows_by_expert(a_q, a_s, w_q, w_s, offsets):
+    """oracle.gemm_fp8 over every row, computed per group of experts in threads (each group is
+    the plain serial computation of its own expert segments)."""
+    import oracle
+
+    E = w_q.shape[0]
+    groups = [g for g in np.array_split(np.arange(E), oracle_threads()) if g.size]
+
+    def part(g):
+        e0, e1 = int(g[0]), int(g[-1]) + 1
+        r0, r1 = int(offsets[e0]), int(offsets[e1])
+        return oracle.gemm_fp8(a_q[r0:r1], a_s[:, r0:r1], w_q[e0:e1], w_s[e0:e1],
+                               offsets[e0:e1 + 1] - r0)
+
+    with cf.ThreadPoolExecutor(max_workers=len(groups)) as ex:
+        return np.concatenate(list(ex.map(part, groups)))

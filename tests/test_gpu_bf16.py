@@ -13,7 +13,8 @@ import torch
 import oracle as orc
 from mixture_experts_layer_softcap_amd import moe, synth
 
-from gpu_util import assert_bf16_close, bf16_f64, to_dev, to_np, zeros
+from gpu_util import (assert_bf16_close, bf16_f64, oracle_rows_parallel, to_dev, to_np,
+                      zeros)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +140,43 @@ def test_bf16_gemm_full_up_projection_sampled():
     assert_f32_close(y[rl], ref, "up projection sample")
 
 
+def test_bf16_gemm_five_panels_ragged_tile_groups():
+    # N = 1280 is five 256-column panels, so a tile group of 4 panels leaves a 1-panel group
+    # per chunk run; 9 chunks are not a multiple of the 8-chunk groups either.  Full output.
+    counts = [700, 0, 1100, 1]          # 3 + 0 + 5 + 1 chunks of up to 256 rows
+    rows, E, N, K = sum(counts), 4, 1280, 256
+    d = inputs(rows, E, N, K, "balanced", seed=21, counts=counts)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_F32)
+    _, ref = oracle_rows_parallel(orc.gemm_bf16, np.arange(rows, dtype=np.int32), d["A"],
+                                  d["W"], d["offsets"])
+    assert_f32_close(y, ref, "N=1280")
+
+
+def chunk_edge_rows(counts, chunk=CHUNK):
+    """Sorted rows at every chunk's first and last row (which covers every expert's first
+    and last row): every task and every tile group of the launch is touched."""
+    off = np.concatenate([[0], np.cumsum(counts)])
+    pick = []
+    for e, c in enumerate(counts):
+        for b in range(0, int(c), chunk):
+            pick += [int(off[e]) + b, int(off[e]) + min(b + chunk, int(c)) - 1]
+    return np.unique(np.array(pick, np.int32))
+
+
+@pytest.mark.parametrize("proj", ["up", "down"])
+@pytest.mark.parametrize("rows,dist", [(29446, "random"), (65536, "skewed")])
+def test_bf16_gemm_bench_sizes(rows, dist, proj):
+    # the timed shapes (E=16, H=3072, I=1536): gated-up [rows,3072]x[3072,3072] and down
+    # [rows,1536]x[1536,3072]; fp32 rows at every chunk boundary against the oracle
+    N, K = (3072, 3072) if proj == "up" else (3072, 1536)
+    d = inputs(rows, 16, N, K, dist, seed=0)
+    y = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_F32)
+    rl = chunk_edge_rows(d["counts"])
+    _, ref = oracle_rows_parallel(orc.gemm_bf16, rl, d["A"], d["W"], d["offsets"])
+    assert_f32_close(y[rl], ref, f"{proj} rows={rows} {dist}")
+    assert np.isfinite(y).all()
+
+
 # ---- the Mixtral-like expert FFN layer ------------------------------------------------
 
 def test_sort_gather_bf16_copies_rows_into_segments():
@@ -183,11 +221,32 @@ def test_ffn_layer_small_full(chunk):
     assert_bf16_close(y, ref, f"ffn chunk={chunk}")
 
 
-def test_ffn_layer_mixtral_shape_sampled():
-    # T=8192 tokens, E=8, top-2, hidden 4096, FFN 1024, skewed router (-1.1 ln(e+1) bias)
-    T, E, k, H, F = 8192, 8, 2, 4096, 1024
+def ffn_ws_part(ws, T, E, k, H, F, which, dtype, n):
+    off = moe.ffn_workspace_offset(T, E, k, H, F, which)
+    return to_np(ws[off:off + n * np.dtype(dtype).itemsize]).view(dtype)
+
+
+@pytest.mark.parametrize("T", [8192, 32768])
+def test_ffn_layer_mixtral_shape_chunk_edges(T):
+    # E=8, top-2, hidden 4096, FFN 1024, skewed router (-1.1 ln(e+1) bias): every token whose
+    # route sits at a chunk's first or last sorted row (both GEMMs' tasks cut the same
+    # chunks), plus a seeded spread, against the oracle
+    E, k, H, F = 8, 2, 4096, 1024
     d = synth.ffn_inputs(T, E, H, F, seed=0)
-    y = run_ffn(d, k)
-    tok = np.random.default_rng(1).choice(T, 48, replace=False).astype(np.int32)
-    _, ref = orc.ffn_tokens(d["logits"], d["x"], d["w_up"], d["w_down"], k, 30.0, tokens=tok)
-    assert_bf16_close(y[tok], ref, "ffn sample")
+    logits, x, wu, wd = d["logits"], d["x"], d["w_up"], d["w_down"]
+    ws = torch.empty(moe.ffn_workspace_bytes(T, E, k, H, F), dtype=torch.uint8, device="cuda")
+    out = zeros((T, H), torch.int16)
+    moe.ffn_forward(to_dev(logits), to_dev(x), to_dev(wu), to_dev(wd), k, 30.0, out, ws)
+    torch.cuda.synchronize()
+    y = to_np(out, np.uint16)
+    ids, _ = orc.route(logits, k, 30.0)
+    counts, offsets = orc.layout(ids, E)
+    np.testing.assert_array_equal(ffn_ws_part(ws, T, E, k, H, F, 2, np.int32, E), counts)
+    np.testing.assert_array_equal(ffn_ws_part(ws, T, E, k, H, F, 3, np.int32, E + 1), offsets)
+    srt = ffn_ws_part(ws, T, E, k, H, F, 8, np.int32, T * k)
+    edges = chunk_edge_rows(counts)
+    tok = np.unique(np.concatenate([srt[edges] // k,
+                                    np.random.default_rng(1).choice(T, 32, replace=False)]))
+    tok = tok.astype(np.int32)
+    _, ref = oracle_rows_parallel(orc.ffn_tokens, tok, logits, x, wu, wd, k, 30.0)
+    assert_bf16_close(y[tok], ref, f"ffn T={T} ({tok.size} tokens)")

@@ -23,7 +23,8 @@ import torch
 import oracle as orc
 from mixture_experts_layer_softcap_amd import moe, synth
 
-from gpu_util import REL_FRO, bf16_f64, to_dev, to_np, zeros
+from gpu_util import (REL_FRO, assert_bf16_close, bf16_f64, oracle_gemm_rows_by_expert,
+                      oracle_rows_parallel, to_dev, to_np, zeros)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,16 +164,66 @@ def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
     np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), offsets)
 
 
-def test_mlp_forward_full_size_sampled():
+def e4m3_rank(codes):
+    """Position of an E4M3FN code on the number line (codes of one sign are monotone in their
+    low 7 bits; -0 and +0 share rank 0), so one rounding step apart is a rank difference 1."""
+    c = codes.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def test_mlp_forward_full_size():
     # the FP8 tutorial's layer as a full expert MLP: M=128, 256 experts, top-8, hidden 2048,
-    # expert width 512 (gate+up 1024 columns)
+    # expert width 512 (gate+up 1024 columns).  Every token against the oracle, then the
+    # reason for the relaxed per-element bar made visible:
+    #  1. the device's activation codes differ from the oracle's only by single E4M3 rounding
+    #     steps, on a small fraction of codes (the gate+up rows carry the matrix core's error);
+    #  2. fed the device's own activation codes and scales, the oracle's down projection and
+    #     combine reproduce the device output to the strict BF16 bar (5e-3 relative Frobenius
+    #     and 2e-2 rms for every element), so nothing but those flips separates the two.
     d = synth.mlp_inputs(**{kk: v for kk, v in
                             synth.MLP_WORKLOADS["mlp_fp8_M128_E256_k8_H2048_I512"].items()})
-    assert moe.mlp_forward_kernels(d["M"], d["E"], d["k"], d["H"], d["I"]) == 6
-    outs, _ = gpu_mlp(d, reps=2)
-    g = np.random.default_rng(0)
-    toks = np.unique(np.concatenate([[0, d["M"] - 1], g.choice(d["M"], 14, replace=False)]))
-    _, y64 = orc.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
-                            d["k"], CAP, tokens=toks.astype(np.int32))
-    assert_mlp_close(outs[0][toks], y64, "mlp full size")
+    M, E, k, H, I = d["M"], d["E"], d["k"], d["H"], d["I"]
+    assert moe.mlp_forward_kernels(M, E, k, H, I) == 6
+    outs, ws = gpu_mlp(d, reps=2)
     np.testing.assert_array_equal(outs[1], outs[0])
+    toks = np.arange(M, dtype=np.int32)
+    _, y64 = oracle_rows_parallel(orc.mlp_tokens, toks, d["logits"], d["x"], d["w1_q"],
+                                  d["w1_s"], d["w2_q"], d["w2_s"], k, CAP)
+    assert_mlp_close(outs[0], y64, "mlp full size")
+
+    R = M * k
+    ids, wts = orc.route(d["logits"], k, CAP)
+    counts, offsets = orc.layout(ids, E)
+    q, sc = orc.quant_act(d["x"])
+    r_ids, xq_s, xs_s = orc.sort_gather(ids, offsets, q, sc)
+    h = oracle_gemm_rows_by_expert(xq_s, xs_s, d["w1_q"], d["w1_s"], offsets)  # sorted order
+    act = orc.swiglu_f32(h)
+    r_codes, r_scales = orc.quant_rows_f32(act)                 # [R][I], [R][I/128]
+    # the device's activations are in route order (small-batch path)
+    g_codes = ws_part(ws, d, 13, np.uint8, R * I).reshape(R, I)[r_ids]
+    g_scales = ws_part(ws, d, 14, np.float32, (I // 128) * R).reshape(I // 128, R)[:, r_ids]
+    np.testing.assert_allclose(g_scales.T, r_scales, rtol=2.0 ** -10, atol=0)
+    # Codes differ only by rounding: the dequantised activations differ by at most one E4M3
+    # step of the oracle's value plus the gate+up rows' own error, which the matrix core
+    # bounds relative to sum |x_i w_i| rather than to the value: near zero that spans several
+    # of the small steps, but stays far below the block's amax (2^-9 of it).
+    table = orc.e4m3_decode_table()
+    mag = r_codes & 0x7F
+    spacing = np.where(mag < 0x7E, np.abs(table[np.minimum(mag + 1, 0x7E)] - table[mag]),
+                       table[0x7E] - table[0x7D])
+    sg = np.repeat(g_scales.T, 128, axis=1)
+    sr = np.repeat(r_scales, 128, axis=1)
+    excess = np.abs(table[g_codes] * sg - table[r_codes] * sr) - spacing * sr
+    amax = 448.0 * sr
+    worst = float(np.max(excess / np.where(amax > 0, amax, 1.0)))
+    step = np.abs(e4m3_rank(g_codes) - e4m3_rank(r_codes))
+    flips = float((step > 0).mean())
+    print(f"activation codes: {flips:.5f} differ, {float((step > 1).mean()):.6f} by more than "
+          f"one step; worst excess over one step 2^{np.log2(max(worst, 2.0 ** -60)):.1f} of "
+          f"the block amax")
+    assert worst <= 2.0 ** -9, "an activation code beyond rounding of the oracle's value"
+    assert flips <= 1e-2, f"{flips:.4f} of the activation codes differ"
+    C2 = oracle_gemm_rows_by_expert(g_codes, g_scales, d["w2_q"], d["w2_s"], offsets)
+    _, y_dev_act = orc.scatter(C2, r_ids, wts, M)
+    assert_bf16_close(outs[0], y_dev_act, "mlp with the device's activation codes")

@@ -5,6 +5,7 @@ GEMM pins reduce the method to exact integer matmuls (numpy int64), to dense flo
 matmuls of the dequantised operands (E=1, k=1), and to sums over every expert (k=E).
 """
 import numpy as np
+import scipy.special
 import pytest
 import torch
 
@@ -92,12 +93,16 @@ def test_quant_weights_blocks_are_128_by_128(orc):
     assert q[1, 130, 300] == 0x7E
     amax = np.abs(w).reshape(2, 2, 128, 3, 128).max(axis=(2, 4))
     np.testing.assert_array_equal(s, (amax / np.float32(448.0)).astype(np.float32))
-    # codes of each block equal the activation quantiser's codes when every row of the block
-    # is forced to share the block amax (it then has the same scale)
-    blk = w[0, :128, :128].copy()
+    # codes of a block equal the activation quantiser's codes when every row of the block is
+    # forced to share the block amax (each row then has the block's scale); the values are
+    # made bf16-exact first so that both quantisers see the same numbers
+    blk = synth.bf16_to_f32(synth.bf16_bits(w[0, :128, :128]))
     blk[:, 0] = np.abs(blk).max()
     qb, sb = orc.quant_weights(np.ascontiguousarray(blk)[None])
-    assert (qb[0].reshape(128, 128) & 0x7F).max() == 0x7E
+    qa, sa = orc.quant_act(synth.bf16_bits(blk))
+    assert sa.shape == (128, 1) and (sa[:, 0] == sb[0, 0, 0]).all()
+    np.testing.assert_array_equal(qb[0], qa)
+    assert (qb[0] & 0x7F).max() == 0x7E
 
 
 # ---- grouped GEMM ---------------------------------------------------------------------
@@ -227,6 +232,38 @@ def test_ffn_single_expert_matches_torch_composition(orc):
     # move a rare tie by one bf16 ulp, so compare with a bound of one ulp per term
     np.testing.assert_allclose(y64, ref.numpy(), rtol=2e-2, atol=1e-3)
     np.testing.assert_allclose(y64, ref.numpy(), rtol=0, atol=np.abs(ref.numpy()).max() * 1e-2)
+
+
+def test_ffn_activation_is_rounded_to_bf16_before_the_down_projection(orc):
+    # One token, one expert (k = 1, weight exactly 1), x = e_0, so g_f and u_f are single
+    # bf16 weights; the down projection is the identity on the first F outputs.  Then
+    # y64[f] is the activation the layer feeds the down GEMM: it must be a bf16 value (the
+    # intermediate rounding of the Mixtral-like layer) within half a bf16 ulp of
+    # silu(g)*u, which scipy's logistic gives independently.  None of the chosen products is
+    # a bf16 value, so an oracle that dropped the rounding would fail the bf16-value checks.
+    H, F = 8, 4
+    g = np.array([0.5, 1.25, -2.0, 3.0], np.float32)
+    u = np.array([1.0, 0.75, 1.5, -0.625], np.float32)
+    x = np.zeros((1, H), np.float32)
+    x[0, 0] = 1.0
+    w_up = np.zeros((1, 2 * F, H), np.float32)
+    w_up[0, :F, 0] = g
+    w_up[0, F:, 0] = u
+    w_down = np.zeros((1, H, F), np.float32)
+    w_down[0, np.arange(F), np.arange(F)] = 1.0
+    logits = np.zeros((1, 1), np.float32)
+    y, y64 = orc.ffn_tokens(logits, synth.bf16_bits(x), synth.bf16_bits(w_up),
+                            synth.bf16_bits(w_down), 1, 30.0)
+    exact = g.astype(np.float64) * scipy.special.expit(g.astype(np.float64)) * u
+    act = y64[0, :F]
+    assert (y64[0, F:] == 0).all()
+    # a bf16 value: exact in fp32 with the low 16 bits of its fp32 image clear
+    assert (act.astype(np.float32).astype(np.float64) == act).all()
+    assert (act.astype(np.float32).view(np.uint32) & 0xFFFF == 0).all()
+    assert (np.abs(act - exact) <= 2.0 ** -8 * np.abs(exact)).all()   # half an ulp (p = 8)
+    # the unrounded products are not bf16 values, so the rounding is what the checks see
+    assert (exact.astype(np.float32).view(np.uint32) & 0xFFFF != 0).all()
+    assert (np.abs(act - exact) > 2.0 ** -20 * np.abs(exact)).all()
 
 
 def test_ffn_k2_weights_combine_two_experts(orc):
