@@ -15,8 +15,10 @@
  *
  * Conventions that hold for every entry point:
  *   - Every pointer argument is DEVICE memory owned by the caller, except where a comment
- *     says "host".  The library never allocates, frees or synchronises inside these calls
- *     (moe_forward's first call for a given shape builds and caches a graph, see there).
+ *     says "host".  The library never allocates, frees or synchronises inside these calls,
+ *     with one opt-in exception: moe_forward_ex with MOE_FWD_GRAPH captures the step on a
+ *     stream of its own (created on first use) and instantiates and caches a graph per
+ *     argument set.  moe_forward and every other entry point launch plain kernels only.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and is
  *     asynchronous; calls made under stream capture are recorded like any other launch.
  *   - Arrays are row-major, last index contiguous.  bf16 travels as uint16_t bit patterns;
@@ -273,6 +275,21 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
 /* Number of kernels moe_forward_ex launches for these arguments: 3 (small batch) or 5 (the
  * gathering path or the staged one); MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
+
+/* ---- the whole step for callers that cannot allocate ----------------------------------
+ * For code that may not call hipMalloc or take a workspace from an allocator (HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  moe_forward with the
+ * library's own scratch in place of the caller's workspace: a 16 MiB device array that each
+ * GPU the library runs on holds from its first use until the process ends, enough for every
+ * shape whose moe_forward_workspace_bytes(...) is at most 16 MiB (the M=128, E=256, top-8,
+ * K=2048, N=512 layer needs 4.4 MiB).  Larger shapes return MOE_E_NOSPC and launch nothing.
+ * Same kernels, same default options and same results as moe_forward; plain launches on
+ * `stream`, no allocation, no host synchronisation.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (other streams, other threads) race, so a
+ * caller serialises them on one stream.  Each call clears what it needs cleared itself. */
+int moe_forward_noalloc(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                        const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                        uint16_t* out, moe_stream_t stream);
 
 /* ---- [WEAVE] / [H200] Mixtral-like expert FFN layer, BF16 --------------------------------
  * route (softcap, top-k) -> layout over many workgroups (chunk_rows rows per task, 0 = 256;

@@ -23,6 +23,7 @@ struct DevState {
     int checked = 0;   // 0 unknown, 1 gfx950, -1 not usable
     DeviceInfo info{0};
     hipStream_t capture = nullptr;
+    void* scratch = nullptr;   // this device's copy of `scratch` (moe_forward_noalloc)
 };
 DevState g_dev[kMaxDevices];
 std::mutex g_mu;
@@ -243,6 +244,32 @@ int forward_graph(const FwdArgs& a, hipStream_t s) {
     }
     g_graphs.push_back(GraphEntry{dev, a, exec});
     return hip_status(hipGraphLaunch(exec, s));
+}
+
+// ---- scratch of the no-allocation forward ------------------------------------------------
+// moe_forward_noalloc's workspace: a file-scope device array, one copy per GPU the library
+// runs on, held until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is a stand-in, not a device address): the address of the current device's
+// copy is looked up once per device and kept in DevState::scratch.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The current device's scratch address (check_device() has set t_dev to that device).
+int noalloc_scratch(void** out) {
+    DevState& d = g_dev[t_dev];
+    if (!d.scratch) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!d.scratch) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return MOE_E_HIP;
+            }
+            d.scratch = p;
+        }
+    }
+    *out = d.scratch;
+    return MOE_OK;
 }
 
 }  // namespace
@@ -573,6 +600,25 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
                 uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
     return moe_forward_ex(logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
                           workspace_bytes, 0, 0, stream);
+}
+
+int moe_forward_noalloc(const float* logits, const uint16_t* x, const uint8_t* w_q,
+                        const float* w_scales, int M, int E, int k, int K, int N, float softcap,
+                        uint16_t* out, moe_stream_t stream) {
+    if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
+    if (!logits || !x || !w_q || !w_scales || !out) return MOE_E_INVAL;
+    if (softcap != softcap) return MOE_E_INVAL;
+    if (ws_layout(M, E, k, K, N).total > kNoAllocScratchBytes) return MOE_E_NOSPC;
+    int rc = check_device();
+    if (rc) return rc;
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws)) != MOE_OK) return rc;
+    // the same kernels as moe_forward, plain launches; each path clears what it accumulates
+    // into (the route kernel zeroes the layout's counters, the layout resets the queue), so
+    // whatever the last call left in the scratch does not matter
+    FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, ws,
+              default_chunk(M, k, E, K), 0};
+    return hip_status(enqueue_forward(a, (hipStream_t)stream));
 }
 
 // ---- Mixtral-like expert FFN layer (BF16) ---------------------------------------------

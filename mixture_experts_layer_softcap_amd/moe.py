@@ -55,6 +55,7 @@ SIGNATURES = {
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _I, _P]),
+    "moe_forward_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "moe_ffn_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_ffn_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _P]),
@@ -231,6 +232,14 @@ def forward(logits, x, w_q, w_scales, k: int, softcap: float, out, workspace,
     _call("moe_forward_ex", _ptr(logits), _ptr(x), _ptr(w_q), _ptr(w_scales), M, E, k, K, N,
           softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
           chunk_rows, flags, _stream(stream))
+
+
+def forward_noalloc(logits, x, w_q, w_scales, k: int, softcap: float, out, stream=None):
+    M, E = logits.shape
+    K = x.shape[1]
+    N = w_q.shape[1]
+    _call("moe_forward_noalloc", _ptr(logits), _ptr(x), _ptr(w_q), _ptr(w_scales), M, E, k, K,
+          N, softcap, _ptr(out), _stream(stream))
 
 
 def sort_gather_bf16(x, topk_ids, E: int, cursors, sorted_route_ids, a, route_slots=None,

@@ -160,3 +160,16 @@ def test_no_gpu_gives_a_device_status():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert moe.lib().moe_device_check() == moe.MOE_E_DEVICE
+
+
+def test_forward_noalloc_rejects_on_the_host(L):
+    # the no-allocation forward: bad arguments, and layers whose workspace exceeds its 16 MiB
+    # scratch, are refused before any HIP call (so also without a GPU)
+    INVAL, NOSPC = moe.MOE_E_INVAL, moe.MOE_E_NOSPC
+    na = L.moe_forward_noalloc
+    assert L.moe_forward_workspace_bytes(1024, 256, 8, 2048, 512) > 16 << 20
+    assert na(P, P, P, P, 1024, 256, 8, 2048, 512, 30.0, P, S) == NOSPC
+    assert na(P, P, P, P, 8, 16, 2, 250, 256, 30.0, P, S) == INVAL       # K % 128
+    assert na(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, S) == INVAL    # null weights
+    assert na(P, P, P, P, 8, 16, 2, 256, 256, 30.0, NULL, S) == INVAL    # null out
+    assert na(P, P, P, P, 8, 16, 2, 256, 256, float("nan"), P, S) == INVAL
