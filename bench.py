@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+SCHEDS = {"auto": -1, "dispatch": 0, "static": 1, "queue": 2, "queue_xcd": 3}
 WEIGHT_BYTES_ROTATION = 1 << 30
 
 
@@ -39,6 +40,10 @@ def parse():
     p.add_argument("--static-grid", action="store_true",
                    help="walk the task list with a fixed stride instead of the atomic queue")
     p.add_argument("--chunk-rows", type=int, default=0)
+    p.add_argument("--sched", default="auto", choices=list(SCHEDS),
+                   help="task schedule of the LDS-tiled grouped GEMMs: hardware dispatch of one "
+                        "workgroup per task, a static persistent walk, one atomic queue, or "
+                        "per-XCD atomic queues (auto: the library's default)")
     p.add_argument("--graph", action="store_true",
                    help="replay the cached HIP graph of the step instead of launching its kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -140,14 +145,14 @@ def bench_bf16_gemm(args, moe, synth, torch, np):
     nb = N // moe.gemm_n_tile(moe.MOE_GEMM_BF16)
     mt = moe.max_tasks(rows, 1, E, nb, chunk)
     z = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)
-    cnt, off, cur, ntasks, queue = z(E), z(E + 1), z(E), z(1), z(2)
+    cnt, off, cur, ntasks, queue = z(E), z(E + 1), z(E), z(1), z(moe.MOE_QUEUE_WORDS)
     tasks = z(mt * 4).view(mt, 4)
     moe.build_layout(ids, E, nb, chunk, cnt, off, cur, tasks, ntasks, queue)
     out = torch.empty((rows, N), dtype=torch.int16, device=dev)
 
     def step(i):
         moe.grouped_gemm(moe.MOE_GEMM_BF16, a, None, ws[i % copies], None, tasks, ntasks, chunk,
-                         out, moe.MOE_EPI_STORE_BF16)
+                         out, moe.MOE_EPI_STORE_BF16, queue=queue, sched=SCHEDS[args.sched])
 
     for i in range(max(args.warmup, copies)):
         step(i)
@@ -173,6 +178,7 @@ def bench_bf16_gemm(args, moe, synth, torch, np):
         "data": "synthetic",
         "config": {"workload": args.workload, "rows": rows, "E": E, "N": N, "K": K,
                    "row_distribution": dist, "nonempty_experts": nonempty, "chunk_rows": chunk,
+                   "sched": args.sched,
                    "max_expert_rows": int(counts.max()), "weight_copies_rotated": copies},
         "effective_tflops": round(tflops, 2),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
@@ -201,9 +207,11 @@ def bench_ffn(args, moe, synth, torch, np):
     logits, x, wu, wd = tl(d["logits"]), tl(d["x"]), tl(d["w_up"]), tl(d["w_down"])
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
     ws = torch.empty(moe.ffn_workspace_bytes(T, E, k, H, F), dtype=torch.uint8, device=dev)
+    sched = SCHEDS[args.sched]
 
     def step(i):
-        moe.ffn_forward(logits, x, wu, wd, k, synth.SOFTCAP, out, ws, chunk_rows=args.chunk_rows)
+        moe.ffn_forward(logits, x, wu, wd, k, synth.SOFTCAP, out, ws, chunk_rows=args.chunk_rows,
+                        flags=moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0)
 
     for i in range(args.warmup):
         step(i)
@@ -230,6 +238,7 @@ def bench_ffn(args, moe, synth, torch, np):
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "E": E, "top_k": k, "hidden": H,
                    "ffn": F, "chunk_rows": args.chunk_rows or 256, "skewed_router": skewed,
+                   "sched": args.sched,
                    "rows_per_expert_max_min": [int(counts.max()), int(counts.min())]},
         "effective_tflops": round(tflops, 2),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
@@ -300,7 +309,7 @@ def bench_mlp(args, moe, synth, torch, np):
         tasks = wsp(5, torch.int32, 4 * mtu).view(mtu, 4)
         nt = wsp(7, torch.int32, 1)
         o7 = moe.mlp_workspace_offset(M, E, k, H, I, 7)
-        queue = ws[o7 + 16:o7 + 24].view(torch.int32)
+        queue = ws[o7 + 64:o7 + 64 + 4 * moe.MOE_QUEUE_WORDS].view(torch.int32)
         sorted_ids = wsp(8, torch.int32, R)
 
         def gemm(i):
@@ -390,7 +399,7 @@ def staged_gemm(args, moe, torch, wsp, M, E, k, K, N, chunk, wqs, wss, copies, r
     max_tasks = moe.max_tasks(M, k, E, N // 128, chunk)
     tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
     ntasks = wsp(6, torch.int32, 1)
-    queue = None if args.static_grid else wsp(7, torch.int32, 2)
+    queue = None if args.static_grid else wsp(7, torch.int32, moe.MOE_QUEUE_WORDS)
     sorted_ids = wsp(8, torch.int32, R)
 
     def gemm(i):
@@ -452,8 +461,10 @@ def main():
     wss = [ws0] + [ws0.clone() for _ in range(copies - 1)]
     out = torch.empty((M, N), dtype=torch.int16, device=dev)
     ws = torch.empty(moe.forward_workspace_bytes(M, E, k, K, N), dtype=torch.uint8, device=dev)
+    sched = SCHEDS[args.sched]
     flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
-        (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0)
+        (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0) | \
+        (moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -501,10 +512,11 @@ def main():
         tasks = wsp(5, torch.int32, 4 * max_tasks).view(max_tasks, 4)
         ntasks = wsp(6, torch.int32, 1)
         sorted_ids = wsp(8, torch.int32, R)
+        queue = wsp(7, torch.int32, moe.MOE_QUEUE_WORDS)
 
         def gemm(i):
             moe.grouped_gemm_gather(x_q, x_s, k, wqs[i % copies], wss[i % copies], tasks, ntasks,
-                                    chunk, sorted_ids, rows_out)
+                                    chunk, sorted_ids, rows_out, queue=queue, sched=sched)
     elif fused:
         # the step's GEMM reads the routed ids (workspace part 0, written by its route stage)
         ids_ws = wsp(0, torch.int32, R).view(M, k)
@@ -570,7 +582,7 @@ def main():
                                       if 64 < chunk <= 256 and K <= 8192
                                       else "static stride" if args.static_grid else "atomic queue"),
                    "launch": "graph" if args.graph else "plain",
-                   "chunk_rows": chunk},
+                   "chunk_rows": chunk, "sched": args.sched if gather else None},
         "effective_tflops": round(flops / (us_layer * 1e-6) / 1e12, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
         "layer_hbm_frac": round(lbytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

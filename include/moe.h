@@ -47,6 +47,27 @@ extern "C" {
 
 typedef void* moe_stream_t; /* hipStream_t */
 
+/* Words of a grouped-GEMM task-counter buffer (`queue` arguments): per-XCD tickets, an exit
+ * count and an error word.  Zero before first use; every launch leaves it zeroed. */
+#define MOE_QUEUE_WORDS 16
+
+/* Task schedules of the LDS-tiled grouped GEMMs (BF16, and FP8 with chunks of 65..256 rows)
+ * ([WEAVE] sections 1.2, 2.2, 3.1 and 4.2):
+ *   MOE_SCHED_DISPATCH   one workgroup per task; the hardware dispatcher hands workgroups to
+ *                        CUs as they free up (in order, round robin over the 8 XCDs)
+ *   MOE_SCHED_STATIC     one workgroup per CU, each walking a fixed share of its XCD's
+ *                        tasks (the static big kernel)
+ *   MOE_SCHED_QUEUE      one workgroup per CU pulling tasks from one atomic counter
+ *   MOE_SCHED_QUEUE_XCD  one workgroup per CU pulling from its XCD's own counter over that
+ *                        XCD's run of tasks, then from the other XCDs' counters
+ * The queue forms need a MOE_QUEUE_WORDS counter buffer.  MOE_SCHED_AUTO picks the measured
+ * fastest for the shape. */
+#define MOE_SCHED_AUTO (-1)
+#define MOE_SCHED_DISPATCH 0
+#define MOE_SCHED_STATIC 1
+#define MOE_SCHED_QUEUE 2
+#define MOE_SCHED_QUEUE_XCD 3
+
 /* One unit of grouped-GEMM work ([WEAVE] section 4.2): rows [row_begin, row_begin+row_count)
  * of expert `expert`'s segment, times the weight panel n_block (n_tile output columns). */
 typedef struct moe_task {
@@ -105,7 +126,7 @@ int moe_max_tasks(int M, int k, int E, int n_blocks, int chunk_rows);
  *                        each chunk crossed with n_blocks weight panels; full chunks first,
  *                        then the partial ones by decreasing row count (largest first)
  *   ntasks s32 [1]       number of tasks written
- *   queue u32 [2]        reset to zero (the grouped GEMM's persistent work queue)
+ *   queue u32 [MOE_QUEUE_WORDS]  reset to zero (the grouped GEMMs' task counters)
  *   sorted_route_ids s32 [M*k]   optional (NULL: not written): the routes in expert order,
  *                        sorted_route_ids[slot] = r for slot in [offsets[e], offsets[e+1])
  *                        of e = topk_ids[r]; the order inside a segment is unspecified
@@ -168,8 +189,8 @@ int moe_gemm_n_tile(int mode);
  * of 64, N a multiple of 256, chunk_rows <= 256; epilogues STORE_F32, STORE_BF16 and
  * SWIGLU_BF16, which writes out [rows][N/2] bf16 = bf16(silu(h[:, c]) * h[:, N/2 + c]) for
  * the task's 128 columns c (weight rows [0, N/2) are the gate, [N/2, N) the up projection).
- * One 256 x 256 output tile per task and workgroup (grid = max_tasks; workgroups past
- * *ntasks exit at once); queue is not used.
+ * One 256 x 256 output tile per task; `sched` (MOE_SCHED_*) picks how tiles reach
+ * workgroups, the queue forms counting in queue (MOE_QUEUE_WORDS words, left zeroed).
  * Scheduling (FP8_B128): for chunk_rows <= 16 and K = 512, 1024 or 2048 the task list is
  * cut into one contiguous range of 16-column subtasks per workgroup, balanced inside the
  * workgroup by an LDS counter; queue is not used.  For chunk_rows in [65, 256] (K <= 8192) one workgroup
@@ -181,12 +202,13 @@ int moe_gemm_n_tile(int mode);
  * the same grid walks the task list with a fixed stride.  Tasks must come from
  * moe_build_layout for the same rows, E, n_tile and chunk_rows (FP8_B128: chunk_rows <= 256):
  * all n_blocks panels of one chunk consecutive.  Each task streams its expert's weight panel
- * once. */
+ * once.  FP8_B128 takes sched = MOE_SCHED_AUTO only (its walk follows queue as above). */
 int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, int K,
                      const void* w, const float* w_scales, int E, int N,
                      const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                      int chunk_rows, uint32_t* queue, int epilogue,
-                     const int32_t* sorted_route_ids, void* out, moe_stream_t stream);
+                     const int32_t* sorted_route_ids, void* out, int sched,
+                     moe_stream_t stream);
 
 /* ---- [FMF8] Baseline items 5-6 with the gather done on load ------------------------------
  * The grouped FP8 GEMM of moe_grouped_gemm (FP8_B128, MOE_EPI_ROUTE_F32) for chunk_rows in
@@ -197,12 +219,15 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
  *                   sum_{kk in block b} e4m3(x_q[t][kk]) * e4m3(w[e][n][kk]),
  * for every route r_id = sorted_route_ids[r] of a task's rows (t = r_id / k, e its expert),
  * rows f32 [M*k][N].  tasks from moe_build_layout (n_tile 128, the same chunk_rows) with its
- * sorted_route_ids.  One workgroup per task pair of one chunk (grid from max_tasks). */
+ * sorted_route_ids.  An item is one chunk against two adjacent panels; `sched` (a
+ * MOE_SCHED_* value) picks how items reach workgroups, the queue forms counting in `queue`
+ * (MOE_QUEUE_WORDS words, zero before the first call, left zeroed; NULL is allowed for
+ * MOE_SCHED_DISPATCH and MOE_SCHED_STATIC). */
 int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, int k, int K,
                             const uint8_t* w, const float* w_scales, int E, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                             int chunk_rows, const int32_t* sorted_route_ids, float* rows,
-                            moe_stream_t stream);
+                            uint32_t* queue, int sched, moe_stream_t stream);
 
 /* ---- [FMF8] Baseline items 2-6 fused: grouped FP8 GEMM straight from routed ids ------------
  * The small-batch GEMM of moe_forward: K = 2048, M*k <= 2048, N a multiple of 128, and E at
@@ -267,6 +292,10 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  *    or route_slots (parts 9, 10, 12) but the token-major x_q and x_scales (13, 14) and the
  *    sort's slot cursors (15). */
 #define MOE_FWD_STAGED 4
+/* bits 3-5: the task schedule of the tiled gathering GEMM, MOE_FWD_SCHED(MOE_SCHED_...);
+ * 0 picks the default.  The queue forms use workspace part 7 as their counters. */
+#define MOE_FWD_SCHED(s) (((s) + 1) << 3)
+#define MOE_FWD_SCHED_MASK (7 << 3)
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
@@ -302,14 +331,16 @@ int moe_forward_noalloc(const float* logits, const uint16_t* x, const uint8_t* w
  * w_down bf16 [E][H][F] -> out bf16 [M][H].  H a multiple of 256, F of 128.  Workspace of
  * moe_ffn_workspace_bytes(...) bytes; parts (for inspection): 0 topk_ids, 1 topk_weights,
  * 2 counts, 3 offsets, 4 cursors, 5 up tasks, 6 down tasks, 7 ntasks, 8 sorted_route_ids,
- * 9 route_slots, 10 per-expert slot cursors of the layout, 11 act, 12 down rows, 13 queue
- * counters.  Six plain launches on `stream`, no host synchronisation. */
+ * 9 route_slots, 10 per-expert slot cursors of the layout, 11 act, 12 down rows, 13 task
+ * counters (MOE_QUEUE_WORDS per GEMM).  Six plain launches on `stream`, no host
+ * synchronisation.  flags: only MOE_FWD_SCHED(...) bits, the schedule of both BF16 GEMMs
+ * (0: the default). */
 size_t moe_ffn_workspace_bytes(int M, int E, int k, int H, int F);
 int64_t moe_ffn_workspace_offset(int M, int E, int k, int H, int F, int which);
 int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up,
                     const uint16_t* w_down, int M, int E, int k, int H, int F, float softcap,
                     uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
-                    moe_stream_t stream);
+                    int flags, moe_stream_t stream);
 
 /* ---- [FMF8] comparison section, "vLLM full MLP" reference, in FP8 ----------------------
  * The activation step of the expert MLP: for each of `rows` rows of h f32 [rows][2I] (gate
@@ -333,7 +364,8 @@ int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_sca
  * [E][H/128][I/128] -> out bf16 [M][H].  H and I positive multiples of 128; chunk_rows as in
  * moe_forward_ex (0 picks it from the batch).  Workspace of moe_mlp_workspace_bytes(...)
  * bytes; parts (for inspection): 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors,
- * 5 gate+up tasks, 6 down tasks, 7 ntasks (gate+up, down) at +0 and queue pairs at +16,
+ * 5 gate+up tasks, 6 down tasks, 7 ntasks (gate+up, down) at +0 and the two GEMMs' task
+ * counters (MOE_QUEUE_WORDS each) at +64,
  * 8 sorted_route_ids, 9 route_slots, 10 x codes (sorted), 11 x scales, 12 gate+up rows f32
  * [M*k][2I], 13 act codes [M*k][I], 14 act scales [I/128][M*k], 15 down rows f32 [M*k][H]
  * at route ids.  Seven plain launches on `stream` (one layout pass writes both task lists),

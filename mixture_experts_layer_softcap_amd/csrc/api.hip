@@ -87,7 +87,7 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
         (size_t)E * 4,              // 4 cursors
         tasks * sizeof(moe_task),   // 5 tasks
         4,                          // 6 ntasks
-        8,                          // 7 queue
+        MOE_QUEUE_WORDS * 4,        // 7 task counters
         R * 4,                      // 8 sorted_route_ids
         R * (size_t)K,              // 9 a_q
         (size_t)(K / 128) * R * 4,  // 10 a_scales
@@ -133,6 +133,21 @@ struct FwdArgs {
     int chunk, flags;
 };
 
+constexpr int kFwdFlagBits = MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED |
+                             MOE_FWD_SCHED_MASK;
+bool fwd_flags_ok(int flags) {
+    return !(flags & ~kFwdFlagBits) && ((flags & MOE_FWD_SCHED_MASK) >> 3) <= 4;
+}
+
+// Task schedule of the forward's tiled gathering GEMM: the one the flags name, else the
+// default for the chunk size (the persistent forms exist for chunks of at most 128 rows).
+int fwd_sched(int flags, int chunk) {
+    const int s = ((flags & MOE_FWD_SCHED_MASK) >> 3) - 1;
+    if (s >= 0) return s;
+    (void)chunk;
+    return MOE_SCHED_DISPATCH;
+}
+
 hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     const WsLayout L = ws_layout(a.M, a.E, a.k, a.K, a.N);
     char* base = static_cast<char*>(a.ws);
@@ -168,7 +183,8 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
             return e;
         if ((e = launch_gemm_fp8_tile_gather(x_q, x_s, a.M, a.k, a.K, a.w_q, a.w_scales, a.N,
                                              tasks, ntasks, max_tasks, a.chunk, sorted, rows,
-                                             s)) != hipSuccess)
+                                             fwd_sched(a.flags, a.chunk), queue, s)) !=
+            hipSuccess)
             return e;
         return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
     }
@@ -298,13 +314,13 @@ FfnLayout ffn_layout(int M, int E, int k, int H, int F) {
         (size_t)E * 4,             // 4 cursors
         tu * sizeof(moe_task),     // 5 tasks of the gated-up GEMM
         td * sizeof(moe_task),     // 6 tasks of the down GEMM
-        16,                        // 7 ntasks (up, down) and two queue pairs
+        16,                        // 7 ntasks (up, down)
         R * 4,                     // 8 sorted_route_ids
         R * 4,                     // 9 route_slots
         (size_t)E * 4,             // 10 per-expert slot cursors of the wide layout
         R * (size_t)F * 2,         // 11 act = silu(gate) * up, bf16 [R][F]
         R * (size_t)H * 4,         // 12 down-projection rows, f32 [R][H]
-        16,                        // 13 queue counters
+        2 * MOE_QUEUE_WORDS * 4,   // 13 task counters of the two GEMMs
     };
     FfnLayout L;
     size_t p = 0;
@@ -338,7 +354,7 @@ MlpLayout mlp_layout(int M, int E, int k, int H, int I) {
         (size_t)E * 4,                // 4 cursors
         tu * sizeof(moe_task),        // 5 gate+up tasks
         td * sizeof(moe_task),        // 6 down tasks
-        32,                           // 7 ntasks (2) at +0, queue pairs (2 x 2) at +16
+        64 + 2 * MOE_QUEUE_WORDS * 4, // 7 ntasks (2) at +0, task counters (2 x 16) at +64
         R * 4,                        // 8 sorted_route_ids
         R * 4,                        // 9 route_slots
         R * (size_t)H,                // 10 x codes, sorted
@@ -469,8 +485,12 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
                      const void* w, const float* w_scales, int E, int N,
                      const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                      int chunk_rows, uint32_t* queue, int epilogue,
-                     const int32_t* sorted_route_ids, void* out, moe_stream_t stream) {
+                     const int32_t* sorted_route_ids, void* out, int sched,
+                     moe_stream_t stream) {
+    if (sched < MOE_SCHED_AUTO || sched > MOE_SCHED_QUEUE_XCD) return MOE_E_INVAL;
     if (mode == MOE_GEMM_BF16) {
+        if ((sched == MOE_SCHED_QUEUE || sched == MOE_SCHED_QUEUE_XCD) && !queue)
+            return MOE_E_INVAL;
         if (rows < 0 || E < 1 || K < 64 || K % 64 || N < 256 || N % 256 || max_tasks < 0)
             return MOE_E_INVAL;
         if (chunk_rows < 1 || chunk_rows > 256) return MOE_E_INVAL;
@@ -484,9 +504,11 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
         if (rc) return rc;
         return hip_status(launch_gemm_bf16(static_cast<const uint16_t*>(a), K,
                                            static_cast<const uint16_t*>(w), N, tasks, ntasks,
-                                           max_tasks, epilogue, out, (hipStream_t)stream));
+                                           max_tasks, epilogue, out, (hipStream_t)stream,
+                                           nullptr, 1, sched, queue));
     }
     if (mode != MOE_GEMM_FP8_B128) return MOE_E_INVAL;
+    if (sched != MOE_SCHED_AUTO) return MOE_E_INVAL;   // FP8: the task walk follows `queue`
     if (rows < 0 || E < 1 || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
         return MOE_E_INVAL;
     if (chunk_rows < 1 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
@@ -524,17 +546,22 @@ int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, in
                             const uint8_t* w, const float* w_scales, int E, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                             int chunk_rows, const int32_t* sorted_route_ids, float* rows,
-                            moe_stream_t stream) {
+                            uint32_t* queue, int sched, moe_stream_t stream) {
     if (!route_dims_ok(M, E, k) || K < 128 || K % 128 || N < 128 || N % 128 || max_tasks < 0)
         return MOE_E_INVAL;
     if (!gemm_fp8_tile_applies(K, chunk_rows)) return MOE_E_INVAL;
     if (!w || !w_scales || !ntasks || !rows || (max_tasks > 0 && !tasks)) return MOE_E_INVAL;
     if (M > 0 && (!x_q || !x_scales || !sorted_route_ids)) return MOE_E_INVAL;
+    if (sched < MOE_SCHED_AUTO || sched > MOE_SCHED_QUEUE_XCD) return MOE_E_INVAL;
+    if (sched == MOE_SCHED_AUTO) sched = fwd_sched(0, chunk_rows);
+    if (sched != MOE_SCHED_DISPATCH && chunk_rows > 128) return MOE_E_INVAL;
+    if ((sched == MOE_SCHED_QUEUE || sched == MOE_SCHED_QUEUE_XCD) && !queue) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
     return hip_status(launch_gemm_fp8_tile_gather(x_q, x_scales, M, k, K, w, w_scales, N, tasks,
                                                   ntasks, max_tasks, chunk_rows,
-                                                  sorted_route_ids, rows, (hipStream_t)stream));
+                                                  sorted_route_ids, rows, sched, queue,
+                                                  (hipStream_t)stream));
 }
 
 int moe_scatter(const float* rows, const int32_t* route_slots, const float* topk_weights,
@@ -566,12 +593,14 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     if (!logits || !x || !w_q || !w_scales || !out || !workspace) return MOE_E_INVAL;
     if (softcap != softcap) return MOE_E_INVAL;
     if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
-    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
+    if (!fwd_flags_ok(flags)) return MOE_E_INVAL;
     if (workspace_bytes < ws_layout(M, E, k, K, N).total) return MOE_E_NOSPC;
+    const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
+    const int sched = ((flags & MOE_FWD_SCHED_MASK) >> 3) - 1;
+    if (sched > MOE_SCHED_DISPATCH && chunk > 128) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
-    FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace,
-              chunk_rows ? chunk_rows : default_chunk(M, k, E, K), flags};
+    FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace, chunk, flags};
     hipStream_t s = (hipStream_t)stream;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
@@ -586,7 +615,7 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags) {
     if (!forward_dims_ok(M, E, k, K, N)) return MOE_E_INVAL;
     if (chunk_rows < 0 || chunk_rows > 256 || (chunk_rows > 64 && K > 8192)) return MOE_E_INVAL;
-    if (flags & ~(MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED)) return MOE_E_INVAL;
+    if (!fwd_flags_ok(flags)) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
@@ -635,11 +664,14 @@ int64_t moe_ffn_workspace_offset(int M, int E, int k, int H, int F, int which) {
 int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up,
                     const uint16_t* w_down, int M, int E, int k, int H, int F, float softcap,
                     uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
-                    moe_stream_t stream) {
+                    int flags, moe_stream_t stream) {
     if (!ffn_dims_ok(M, E, k, H, F)) return MOE_E_INVAL;
     if (!logits || !x || !w_up || !w_down || !out || !workspace) return MOE_E_INVAL;
     if (softcap != softcap) return MOE_E_INVAL;
     if (chunk_rows < 0 || chunk_rows > 256) return MOE_E_INVAL;
+    if ((flags & ~MOE_FWD_SCHED_MASK) || ((flags & MOE_FWD_SCHED_MASK) >> 3) > 4)
+        return MOE_E_INVAL;
+    const int sched = ((flags & MOE_FWD_SCHED_MASK) >> 3) - 1;   // -1: the default
     const FfnLayout L = ffn_layout(M, E, k, H, F);
     if (workspace_bytes < L.total) return MOE_E_NOSPC;
     int rc = check_device();
@@ -673,11 +705,11 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
             hipSuccess ||
         (e = launch_layout_sorted_wide(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu,
                                        nt, queue, rel, sorted, s, slots, nbd, td, nt + 1,
-                                       queue + 2)) != hipSuccess ||
+                                       queue + MOE_QUEUE_WORDS)) != hipSuccess ||
         (e = launch_gemm_bf16(x, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s,
-                              sorted, k)) != hipSuccess ||
-        (e = launch_gemm_bf16(act, F, w_down, H, td, nt + 1, mtd, MOE_EPI_STORE_F32, down, s)) !=
-            hipSuccess ||
+                              sorted, k, sched, queue)) != hipSuccess ||
+        (e = launch_gemm_bf16(act, F, w_down, H, td, nt + 1, mtd, MOE_EPI_STORE_F32, down, s,
+                              nullptr, 1, sched, queue + MOE_QUEUE_WORDS)) != hipSuccess ||
         (e = launch_scatter(down, slots, wts, ids, M, k, E, H, out, s)) != hipSuccess)
         return hip_status(e);
     return MOE_OK;
@@ -745,7 +777,8 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     moe_task* tu = reinterpret_cast<moe_task*>(at(5));
     moe_task* td = reinterpret_cast<moe_task*>(at(6));
     int32_t* nt = reinterpret_cast<int32_t*>(at(7));
-    uint32_t* queue = reinterpret_cast<uint32_t*>(at(7) + 16);
+    uint32_t* queue = reinterpret_cast<uint32_t*>(at(7) + 64);
+    uint32_t* queue2 = queue + MOE_QUEUE_WORDS;
     int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
     int32_t* slots = reinterpret_cast<int32_t*>(at(9));
     uint8_t* xq = reinterpret_cast<uint8_t*>(at(10));
@@ -766,7 +799,7 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
         // order and the down GEMM gathers its rows by sorted route id
         if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
             (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
-                               nt + 1, queue + 2, sorted, nullptr, s)) != hipSuccess ||
+                               nt + 1, queue2, sorted, nullptr, s)) != hipSuccess ||
             (e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s)) !=
                 hipSuccess ||
             (e = launch_swiglu_quant(h1, R, I, aq, as, s)) != hipSuccess ||
@@ -779,13 +812,13 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     }
     if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
         (e = launch_layout2(ids, M, k, E, chunk, counts, offsets, cursors, nbu, tu, nt, queue,
-                            nbd, td, nt + 1, queue + 2, s)) != hipSuccess ||
+                            nbd, td, nt + 1, queue2, s)) != hipSuccess ||
         (e = launch_qsg(x, M, H, ids, k, E, cursors, sorted, slots, xq, xs, s)) != hipSuccess ||
         (e = launch_gemm_fp8(xq, xs, R, H, w1_q, w1_scales, E, 2 * I, tu, nt, mtu, chunk, queue,
                              MOE_EPI_STORE_F32, sorted, h1, s)) != hipSuccess ||
         (e = launch_swiglu_quant(h1, R, I, aq, as, s)) != hipSuccess ||
         (e = launch_gemm_fp8(aq, as, R, I, w2_q, w2_scales, E, H, td, nt + 1, mtd, chunk,
-                             queue + 2, MOE_EPI_ROUTE_F32, sorted, h2, s)) != hipSuccess ||
+                             queue2, MOE_EPI_ROUTE_F32, sorted, h2, s)) != hipSuccess ||
         (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s)) != hipSuccess)
         return hip_status(e);
     return MOE_OK;

@@ -107,8 +107,8 @@ __device__ void write_tasks(int c, int row0, int E, int n_blocks, int chunk,
     }
     if (tid == 0) {
         ntasks[0] = nchunks * n_blocks;
-        queue[0] = 0u;
-        queue[1] = 0u;
+#pragma unroll
+        for (int i = 0; i < MOE_QUEUE_WORDS; ++i) queue[i] = 0u;
     }
 }
 

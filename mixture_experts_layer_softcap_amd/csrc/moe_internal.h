@@ -91,11 +91,14 @@ hipError_t launch_gemm_fp8_tile(const uint8_t* a, const float* a_scales, int row
                                 hipStream_t s);
 // the same with sorted row r read from token sorted[r] / k of x_q [M][K] (scales [K/128][M]);
 // fp32 rows written at route ids
+// (sched: MOE_SCHED_DISPATCH / STATIC / QUEUE / QUEUE_XCD; the queue forms use `queue`,
+// MOE_QUEUE_WORDS zeroed words, which they leave zeroed)
 hipError_t launch_gemm_fp8_tile_gather(const uint8_t* x_q, const float* x_scales, int M, int k,
                                        int K, const uint8_t* w, const float* w_scales, int N,
                                        const moe_task* tasks, const int32_t* ntasks,
                                        int max_tasks, int chunk_rows, const int32_t* sorted,
-                                       float* rows_out, hipStream_t s);
+                                       float* rows_out, int sched, uint32_t* queue,
+                                       hipStream_t s);
 
 // small-batch forward GEMM with the layout, sort/gather and quantisation folded in: weight
 // slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])
@@ -110,10 +113,12 @@ hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* count
 
 // BF16 grouped GEMM (256 x 256 tiles; STORE_F32, STORE_BF16, SWIGLU_BF16)
 // (with sorted != nullptr, A row s is row sorted[s] / kr of a: gathered on load)
+// (sched: MOE_SCHED_*; AUTO picks hardware dispatch; the queue forms count in `queue`)
 hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                             int epilogue, void* out, hipStream_t s,
-                            const int32_t* sorted = nullptr, int kr = 1);
+                            const int32_t* sorted = nullptr, int kr = 1,
+                            int sched = MOE_SCHED_AUTO, uint32_t* queue = nullptr);
 
 // silu(g) * u requantised per 128 columns (the FP8 expert MLP's activation step)
 hipError_t launch_swiglu_quant(const float* h, int R, int I, uint8_t* a_q, float* a_scales,

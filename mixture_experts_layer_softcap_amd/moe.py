@@ -31,6 +31,17 @@ MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
 MOE_FWD_STAGED = 4
 
+MOE_QUEUE_WORDS = 16
+MOE_SCHED_AUTO = -1
+MOE_SCHED_DISPATCH = 0
+MOE_SCHED_STATIC = 1
+MOE_SCHED_QUEUE = 2
+MOE_SCHED_QUEUE_XCD = 3
+
+
+def MOE_FWD_SCHED(s: int) -> int:
+    return (s + 1) << 3
+
 # entry points and their C signatures (names identical to include/moe.h)
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
@@ -45,11 +56,11 @@ SIGNATURES = {
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_gemm_n_tile": (_I, [_I]),
     "moe_grouped_gemm": (_I, [_I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I,
-                              _P, _P, _P]),
+                              _P, _P, _I, _P]),
     "moe_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_grouped_gemm_routed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
     "moe_grouped_gemm_gather": (_I, [_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P,
-                                     _P]),
+                                     _P, _I, _P]),
     "moe_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_forward_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
@@ -58,7 +69,7 @@ SIGNATURES = {
     "moe_forward_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "moe_ffn_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_ffn_workspace_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
-    "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _P]),
+    "moe_ffn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _I, _I, _P]),
     "moe_swiglu_quant": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_mlp_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I]),
@@ -168,23 +179,25 @@ def gemm_n_tile(mode: int) -> int:
 
 
 def grouped_gemm(mode: int, a, a_scales, w, w_scales, tasks, ntasks, chunk_rows: int, out,
-                 epilogue: int, queue=None, sorted_route_ids=None, stream=None):
+                 epilogue: int, queue=None, sorted_route_ids=None, sched: int = MOE_SCHED_AUTO,
+                 stream=None):
     rows, K = a.shape
     E, N, _ = w.shape
     _call("moe_grouped_gemm", mode, _ptr(a), _ptr(a_scales), rows, K, _ptr(w), _ptr(w_scales),
           E, N, _ptr(tasks), _ptr(ntasks), tasks.shape[0], chunk_rows, _ptr(queue), epilogue,
-          _ptr(sorted_route_ids), _ptr(out), _stream(stream))
+          _ptr(sorted_route_ids), _ptr(out), sched, _stream(stream))
 
 
 def grouped_gemm_gather(x_q, x_scales, k: int, w_q, w_scales, tasks, ntasks, chunk_rows: int,
-                        sorted_route_ids, rows, stream=None):
+                        sorted_route_ids, rows, queue=None, sched: int = MOE_SCHED_AUTO,
+                        stream=None):
     """Grouped FP8 GEMM gathering routed rows from token-major codes (moe_grouped_gemm_gather);
     rows f32 [M*k][N] at route ids."""
     M, K = x_q.shape
     E, N, _ = w_q.shape
     _call("moe_grouped_gemm_gather", _ptr(x_q), _ptr(x_scales), M, k, K, _ptr(w_q),
           _ptr(w_scales), E, N, _ptr(tasks), _ptr(ntasks), tasks.shape[0], chunk_rows,
-          _ptr(sorted_route_ids), _ptr(rows), _stream(stream))
+          _ptr(sorted_route_ids), _ptr(rows), _ptr(queue), sched, _stream(stream))
 
 
 def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
@@ -262,13 +275,13 @@ def ffn_workspace_offset(M: int, E: int, k: int, H: int, F: int, which: int) -> 
 
 
 def ffn_forward(logits, x, w_up, w_down, k: int, softcap: float, out, workspace,
-                chunk_rows: int = 0, stream=None):
+                chunk_rows: int = 0, flags: int = 0, stream=None):
     M, E = logits.shape
     H = x.shape[1]
     F = w_down.shape[2]
     _call("moe_ffn_forward", _ptr(logits), _ptr(x), _ptr(w_up), _ptr(w_down), M, E, k, H, F,
           softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-          chunk_rows, _stream(stream))
+          chunk_rows, flags, _stream(stream))
 
 
 def swiglu_quant(h, a_q, a_scales, stream=None):

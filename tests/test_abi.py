@@ -102,42 +102,51 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert rq(P, P, 4, 8, 2, 256, 30.0, P, P, NULL, P, S) == INVAL   # null x_q
     assert rq(P, P, 4, 8, 9, 256, 30.0, P, P, P, P, S) == INVAL      # k > E
     gga = L.moe_grouped_gemm_gather
-    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 64, P, P, S) == INVAL     # chunk <= 64
-    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 257, P, P, S) == INVAL    # chunk > 256
-    assert gga(P, P, 4, 2, 8320, P, P, 8, 256, P, P, 8, 128, P, P, S) == INVAL   # K > 8192
-    assert gga(P, P, 4, 2, 256, P, P, 8, 200, P, P, 8, 128, P, P, S) == INVAL    # N % 128
-    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 128, NULL, P, S) == INVAL # sorted ids
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 64, P, P, P, -1, S) == INVAL     # chunk <= 64
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 257, P, P, P, -1, S) == INVAL    # chunk > 256
+    assert gga(P, P, 4, 2, 8320, P, P, 8, 256, P, P, 8, 128, P, P, P, -1, S) == INVAL   # K > 8192
+    assert gga(P, P, 4, 2, 256, P, P, 8, 200, P, P, 8, 128, P, P, P, -1, S) == INVAL    # N % 128
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 128, NULL, P, P, -1, S) == INVAL # sorted ids
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 128, P, P, NULL, 2, S) == INVAL  # queue
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 256, P, P, P, 3, S) == INVAL  # 256 rows
+    assert gga(P, P, 4, 2, 256, P, P, 8, 256, P, P, 8, 128, P, P, P, 4, S) == INVAL  # sched
     assert L.moe_quant_sort_gather(P, 4, 200, P, 2, 8, P, P, P, P, P, S) == INVAL  # K % 128
     assert L.moe_quant_sort_gather(P, 4, 256, NULL, 2, 8, P, P, P, P, P, S) == INVAL
     assert L.moe_quantize_weights(P, 2, 100, 256, P, P, S) == INVAL
     assert L.moe_quantize_weights(NULL, 2, 128, 256, P, P, S) == INVAL
     gg = L.moe_grouped_gemm
-    assert gg(7, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # mode
-    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 257, P, 0, P, P, S) == INVAL  # chunk
-    assert gg(0, P, P, 4, 8320, P, P, 2, 256, P, P, 8, 65, P, 0, P, P, S) == INVAL  # tiled K
-    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 9, P, P, S) == INVAL  # epilogue
-    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 2, NULL, P, S) == INVAL  # route ids
-    assert gg(0, P, P, 4, 250, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, S) == INVAL  # K % 128
+    assert gg(7, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, -1, S) == INVAL  # mode
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 257, P, 0, P, P, -1, S) == INVAL  # chunk
+    assert gg(0, P, P, 4, 8320, P, P, 2, 256, P, P, 8, 65, P, 0, P, P, -1, S) == INVAL  # tiled K
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 9, P, P, -1, S) == INVAL  # epilogue
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 2, NULL, P, -1, S) == INVAL  # route ids
+    assert gg(0, P, P, 4, 250, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, -1, S) == INVAL  # K % 128
     assert L.moe_scatter(P, P, P, P, 4, 2, 8, 6, P, S) == INVAL       # N % 4
     ws = L.moe_forward_workspace_bytes(8, 16, 2, 256, 256)
     f = L.moe_forward_ex
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC
-    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 8, S) == INVAL     # flags
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 64, S) == INVAL    # flags
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 5 << 3, S) == INVAL  # sched
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 256, moe.MOE_FWD_SCHED(2),
+             S) == INVAL                                                       # 256 rows
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 257, 0, S) == INVAL   # chunk
     assert f(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 0, S) == INVAL
     assert L.moe_forward(P, P, P, P, 0, 16, 2, 256, 256, 30.0, P, P, ws, S) == INVAL
     assert L.moe_sort_gather_bf16(P, 4, 100, P, 2, 8, P, P, P, P, S) == INVAL   # K % 8
-    assert gg(1, P, P, 4, 96, P, P, 2, 256, P, P, 8, 256, P, 1, P, P, S) == INVAL  # K % 64
-    assert gg(1, P, P, 4, 128, P, P, 2, 384, P, P, 8, 256, P, 1, P, P, S) == INVAL  # N % 256
-    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 257, P, 1, P, P, S) == INVAL  # chunk
-    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 256, P, 2, P, P, S) == INVAL  # ROUTE_F32
+    assert gg(1, P, P, 4, 96, P, P, 2, 256, P, P, 8, 256, P, 1, P, P, -1, S) == INVAL  # K % 64
+    assert gg(1, P, P, 4, 128, P, P, 2, 384, P, P, 8, 256, P, 1, P, P, -1, S) == INVAL  # N % 256
+    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 257, P, 1, P, P, -1, S) == INVAL  # chunk
+    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 256, P, 2, P, P, -1, S) == INVAL  # ROUTE_F32
     fw = L.moe_ffn_workspace_bytes(16, 8, 2, 512, 256)
     assert fw > 0 and L.moe_ffn_workspace_bytes(16, 8, 2, 500, 256) == 0         # H % 256
     assert L.moe_ffn_workspace_bytes(16, 8, 2, 512, 200) == 0                    # F % 128
     ff = L.moe_ffn_forward
-    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw - 1, 0, S) == NOSPC
-    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 300, S) == INVAL   # chunk
-    assert ff(P, NULL, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 0, S) == INVAL
+    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw - 1, 0, 0, S) == NOSPC
+    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 300, 0, S) == INVAL   # chunk
+    assert ff(P, NULL, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 0, 0, S) == INVAL
+    assert ff(P, P, P, P, 16, 8, 2, 512, 256, 30.0, P, P, fw, 0, 1, S) == INVAL    # flags
+    assert gg(1, P, P, 4, 128, P, P, 2, 256, P, P, 8, 256, NULL, 1, P, P, 2, S) == INVAL  # queue
+    assert gg(0, P, P, 4, 256, P, P, 2, 256, P, P, 8, 16, P, 0, P, P, 0, S) == INVAL  # FP8 sched
     sq = L.moe_swiglu_quant
     assert sq(P, 4, 200, P, P, S) == INVAL                                       # I % 128
     assert sq(P, -1, 256, P, P, S) == INVAL

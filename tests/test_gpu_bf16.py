@@ -41,23 +41,29 @@ def layout_for_counts(counts, n_blocks, chunk=CHUNK):
     mt = moe.max_tasks(rows, 1, E, n_blocks, chunk)
     dev = dict(counts=zeros((E,), torch.int32), offsets=zeros((E + 1,), torch.int32),
                cursors=zeros((E,), torch.int32), tasks=zeros((max(mt, 1), 4), torch.int32),
-               ntasks=zeros((1,), torch.int32), queue=zeros((2,), torch.int32))
+               ntasks=zeros((1,), torch.int32), queue=zeros((moe.MOE_QUEUE_WORDS,), torch.int32))
     moe.build_layout(to_dev(ids), E, n_blocks, chunk, dev["counts"], dev["offsets"],
                      dev["cursors"], dev["tasks"], dev["ntasks"], dev["queue"])
     return dev
 
 
-def run_gemm(A, W, counts, epilogue, out_cols=None):
+SCHEDS = (moe.MOE_SCHED_DISPATCH, moe.MOE_SCHED_STATIC, moe.MOE_SCHED_QUEUE,
+          moe.MOE_SCHED_QUEUE_XCD)
+
+
+def run_gemm(A, W, counts, epilogue, out_cols=None, sched=moe.MOE_SCHED_AUTO, repeat=1):
     rows, K = A.shape
     E, N, _ = W.shape
     lay = layout_for_counts(counts, N // moe.gemm_n_tile(moe.MOE_GEMM_BF16))
     cols = N if out_cols is None else out_cols
     dt = torch.float32 if epilogue == moe.MOE_EPI_STORE_F32 else torch.int16
     out = zeros((rows, cols), dt)
-    moe.grouped_gemm(moe.MOE_GEMM_BF16, to_dev(A), None, to_dev(W), None, lay["tasks"],
-                     lay["ntasks"], CHUNK, out, epilogue)
+    args = (to_dev(A), None, to_dev(W), None, lay["tasks"], lay["ntasks"], CHUNK, out, epilogue)
+    for _ in range(repeat):
+        moe.grouped_gemm(moe.MOE_GEMM_BF16, *args, queue=lay["queue"], sched=sched)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(lay["counts"]), counts)
+    assert (to_np(lay["queue"]) == 0).all(), "task counters not left zeroed"
     return to_np(out, None if dt == torch.float32 else np.uint16)
 
 
@@ -152,6 +158,28 @@ def test_bf16_gemm_five_panels_ragged_tile_groups():
     assert_f32_close(y, ref, "N=1280")
 
 
+@pytest.mark.parametrize("sched", SCHEDS)
+@pytest.mark.parametrize("epilogue", [moe.MOE_EPI_STORE_F32, moe.MOE_EPI_STORE_BF16,
+                                      moe.MOE_EPI_SWIGLU_BF16])
+def test_bf16_gemm_schedules(epilogue, sched):
+    # each task schedule and epilogue on a skewed split with an empty expert, ragged chunks and
+    # ten k steps (one pass of the six stage phases plus four): the schedule only decides which
+    # workgroup runs a tile, so outputs are bit-identical to hardware dispatch; fp32 rows are
+    # also checked against the oracle; repeated launches reuse the counters
+    counts = [900, 0, 37, 1300, 257]
+    rows, E, N, K = sum(counts), 5, 1024, 640
+    d = inputs(rows, E, N, K, "balanced", seed=31, counts=counts)
+    cols = N // 2 if epilogue == moe.MOE_EPI_SWIGLU_BF16 else None
+    y = run_gemm(d["A"], d["W"], d["counts"], epilogue, out_cols=cols, sched=sched, repeat=2)
+    y0 = run_gemm(d["A"], d["W"], d["counts"], epilogue, out_cols=cols,
+                  sched=moe.MOE_SCHED_DISPATCH)
+    np.testing.assert_array_equal(y, y0)
+    if epilogue == moe.MOE_EPI_STORE_F32:
+        _, ref = oracle_rows_parallel(orc.gemm_bf16, np.arange(rows, dtype=np.int32), d["A"],
+                                      d["W"], d["offsets"])
+        assert_f32_close(y, ref, f"sched={sched}")
+
+
 def chunk_edge_rows(counts, chunk=CHUNK):
     """Sorted rows at every chunk's first and last row (which covers every expert's first
     and last row): every task and every tile group of the launch is touched."""
@@ -175,6 +203,10 @@ def test_bf16_gemm_bench_sizes(rows, dist, proj):
     _, ref = oracle_rows_parallel(orc.gemm_bf16, rl, d["A"], d["W"], d["offsets"])
     assert_f32_close(y[rl], ref, f"{proj} rows={rows} {dist}")
     assert np.isfinite(y).all()
+    if rows == 29446:
+        for sched in SCHEDS[1:]:
+            yq = run_gemm(d["A"], d["W"], d["counts"], moe.MOE_EPI_STORE_F32, sched=sched)
+            np.testing.assert_array_equal(yq, y)
 
 
 # ---- the Mixtral-like expert FFN layer ------------------------------------------------
@@ -239,6 +271,14 @@ def test_ffn_layer_mixtral_shape_chunk_edges(T):
     moe.ffn_forward(to_dev(logits), to_dev(x), to_dev(wu), to_dev(wd), k, 30.0, out, ws)
     torch.cuda.synchronize()
     y = to_np(out, np.uint16)
+    for sched in SCHEDS[1:]:              # every schedule gives the same bits
+        out2 = zeros((T, H), torch.int16)
+        moe.ffn_forward(to_dev(logits), to_dev(x), to_dev(wu), to_dev(wd), k, 30.0, out2, ws,
+                        flags=moe.MOE_FWD_SCHED(sched))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(out2, np.uint16), y)
+        q = ffn_ws_part(ws, T, E, k, H, F, 13, np.uint32, 2 * moe.MOE_QUEUE_WORDS)
+        assert (q == 0).all()
     ids, _ = orc.route(logits, k, 30.0)
     counts, offsets = orc.layout(ids, E)
     np.testing.assert_array_equal(ffn_ws_part(ws, T, E, k, H, F, 2, np.int32, E), counts)

@@ -155,7 +155,8 @@ def gpu_layout(ids, E, n_blocks, chunk):
     mt = moe.max_tasks(M, k, E, n_blocks, chunk)
     counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
     tasks = torch.full((max(mt, 1), 4), -7, dtype=torch.int32, device=DEV)
-    ntasks, queue = zeros(1, torch.int32), torch.full((2,), 5, dtype=torch.int32, device=DEV)
+    ntasks = zeros(1, torch.int32)
+    queue = torch.full((moe.MOE_QUEUE_WORDS,), 5, dtype=torch.int32, device=DEV)
     moe.build_layout(to_dev(ids), E, n_blocks, chunk, counts, offsets, cursors, tasks, ntasks,
                      queue)
     sync()
@@ -207,7 +208,7 @@ def test_layout_sorted_routes(name, chunk):
     mt = moe.max_tasks(M, k, E, nb, chunk)
     counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
     tasks = zeros((mt, 4), torch.int32)
-    ntasks, queue = zeros(1, torch.int32), zeros(2, torch.int32)
+    ntasks, queue = zeros(1, torch.int32), zeros(moe.MOE_QUEUE_WORDS, torch.int32)
     srt = torch.full((M * k,), -5, dtype=torch.int32, device=DEV)
     slots = torch.full((M * k,), -5, dtype=torch.int32, device=DEV)
     moe.build_layout(to_dev(ids), E, nb, chunk, counts, offsets, cursors, tasks, ntasks, queue,
@@ -382,7 +383,7 @@ def gpu_gemm(a_q, a_s, w_q, w_s, offsets, chunk, epilogue, sorted_ids=None, queu
     tasks = orc.tasks(counts, offsets, N // 128, chunk)
     tasks_d = to_dev(tasks if len(tasks) else np.zeros((1, 4), np.int32))
     ntasks = to_dev(np.array([len(tasks)], np.int32))
-    q = zeros(2, torch.int32) if queue else None
+    q = zeros(moe.MOE_QUEUE_WORDS, torch.int32) if queue else None
     n_out = rows if out_rows is None else out_rows
     dt = torch.int16 if epilogue == moe.MOE_EPI_STORE_BF16 else torch.float32
     out = torch.full((n_out, N), -3, dtype=dt, device=DEV)
@@ -488,23 +489,31 @@ def test_gemm_tiled_multi_chunk_epilogues(chunk):
     np.testing.assert_array_equal(rt[perm], ref)
 
 
-def gpu_gemm_gather(x_q, x_s, ids, w_q, w_s, chunk):
-    """moe_build_layout (sorted) + moe_grouped_gemm_gather on device; rows at route ids."""
+SCHEDS = (moe.MOE_SCHED_DISPATCH, moe.MOE_SCHED_STATIC, moe.MOE_SCHED_QUEUE,
+          moe.MOE_SCHED_QUEUE_XCD)
+
+
+def gpu_gemm_gather(x_q, x_s, ids, w_q, w_s, chunk, sched=moe.MOE_SCHED_AUTO, repeat=1):
+    """moe_build_layout (sorted) + moe_grouped_gemm_gather on device; rows at route ids.  The
+    task counters must come back zeroed (and the iteration-cap word clear)."""
     M, k = ids.shape
     E, N, K = w_q.shape
     nb = N // 128
     mt = moe.max_tasks(M, k, E, nb, chunk)
     counts, offsets, cursors = zeros(E, torch.int32), zeros(E + 1, torch.int32), zeros(E, torch.int32)
     tasks = zeros((mt, 4), torch.int32)
-    ntasks, queue = zeros(1, torch.int32), zeros(2, torch.int32)
+    ntasks, queue = zeros(1, torch.int32), zeros(moe.MOE_QUEUE_WORDS, torch.int32)
     srt = zeros(M * k, torch.int32)
     ids_d = to_dev(ids)
     moe.build_layout(ids_d, E, nb, chunk, counts, offsets, cursors, tasks, ntasks, queue,
                      sorted_route_ids=srt)
     rows = torch.full((M * k, N), -3.0, dtype=torch.float32, device=DEV)
-    moe.grouped_gemm_gather(to_dev(x_q), to_dev(x_s), k, to_dev(w_q), to_dev(w_s), tasks, ntasks,
-                            chunk, srt, rows)
+    args = (to_dev(x_q), to_dev(x_s), k, to_dev(w_q), to_dev(w_s), tasks, ntasks, chunk, srt,
+            rows)
+    for _ in range(repeat):
+        moe.grouped_gemm_gather(*args, queue=queue, sched=sched)
     sync()
+    assert (to_np(queue) == 0).all(), "task counters not left zeroed"
     return to_np(rows)
 
 
@@ -542,6 +551,49 @@ def skewed_reference(name):
     _, y64 = oracle_rows_parallel(orc.forward_tokens, toks, d["logits"], d["x"], d["w_q"],
                                   d["w_s"], d["k"], CAP)
     return dict(ids=ids, counts=counts, offsets=offsets, q=q, sc=sc, sorted=r_ids, C=C, y64=y64)
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+@pytest.mark.parametrize("chunk", [96, 128])
+def test_gemm_gather_schedules_integer_exact(chunk, sched):
+    # every task schedule (hardware dispatch, static walk, one queue, per-XCD queues) on
+    # integer codes with power-of-two scales: exact, and repeated launches reuse the counters
+    g = np.random.default_rng(chunk + 7)
+    M, k, E, N, K = 700, 3, 9, 512, 640
+    bias = np.linspace(3.0, -3.0, E).astype(np.float32)
+    logits = (g.standard_normal((M, E)) + bias).astype(np.float32)
+    ids, _ = orc.route(logits, k, CAP)
+    Ai = g.integers(-4, 5, (M, K))
+    Wi = g.integers(-4, 5, (E, N, K))
+    sa = np.exp2(g.integers(-1, 2, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(g.integers(-1, 2, (E, N // 128, K // 128))).astype(np.float32)
+    counts, offsets = orc.layout(ids, E)
+    r_ids, a_q, a_s = orc.sort_gather(ids, offsets, int_codes(Ai), sa)
+    C = orc.gemm_fp8(a_q, a_s, int_codes(Wi), sb, offsets).astype(np.float32)
+    got = gpu_gemm_gather(int_codes(Ai), sa.T.copy(), ids, int_codes(Wi), sb, chunk,
+                          sched=sched, repeat=3)
+    np.testing.assert_array_equal(got[r_ids], C)
+
+
+@pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
+def test_gemm_gather_schedules_agree_on_skewed_layers(name):
+    # the schedules only decide which workgroup runs a tile, so the rows are bit-identical
+    d = workload(name)
+    ref = skewed_reference(name)
+    outs = [gpu_gemm_gather(ref["q"], ref["sc"].T.copy(), ref["ids"], d["w_q"], d["w_s"], 128,
+                            sched=s, repeat=2) for s in SCHEDS]
+    assert_gemm_f32_close(outs[0][ref["sorted"]], ref["C"], name)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_gemm_gather_persistent_schedules_refuse_256_row_chunks():
+    d = workload(ZIPF1K)
+    ref = skewed_reference(ZIPF1K)
+    for s in SCHEDS[1:]:
+        with pytest.raises(moe.MoeError):
+            gpu_gemm_gather(ref["q"], ref["sc"].T.copy(), ref["ids"], d["w_q"], d["w_s"], 256,
+                            sched=s)
 
 
 @pytest.mark.parametrize("chunk", [128, 256])
@@ -739,6 +791,22 @@ def test_forward_skewed_full(name, chunk):
     for o in outs:
         assert_bf16_close(o, ref["y64"], f"{name} chunk={chunk}")
         np.testing.assert_array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
+def test_forward_skewed_schedules(name):
+    # the whole layer under each task schedule of its tiled GEMM: bit-identical outputs
+    d = workload(name)
+    ref = skewed_reference(name)
+    base = None
+    for s in SCHEDS:
+        outs, ws = gpu_forward(d, reps=2, flags=moe.MOE_FWD_SCHED(s), keep_ws=True)
+        assert (ws_part(ws, d, 7, np.uint32, moe.MOE_QUEUE_WORDS) == 0).all()
+        if base is None:
+            base = outs[0]
+            assert_bf16_close(base, ref["y64"], f"{name} sched={s}")
+        for o in outs:
+            np.testing.assert_array_equal(o, base)
 
 
 @pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
