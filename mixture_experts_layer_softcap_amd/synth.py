@@ -200,3 +200,14 @@ def ffn_inputs(T: int, E: int, H: int, F: int, seed: int = 0, skewed: bool = Tru
     return dict(logits=logits, x=x, w_up=w_up, w_down=w_down)
 
 
+
+
+def router_inputs(M: int, H: int, E: int, seed: int = 0):
+    """Hidden states and gate weights of the router projection: x bf16 [M,H] ~ N(0,1) and
+    w_gate bf16 [E,H] ~ N(0, 1/H), so the logits x . w_gate^T have about unit variance like
+    the directly drawn logits of the other workloads."""
+    g = rng(seed)
+    x = bf16_bits(g.standard_normal((M, H), dtype=np.float32))
+    wg = g.standard_normal((E, H), dtype=np.float32)
+    wg *= np.float32(1.0 / np.sqrt(H))
+    return dict(x=x, w_gate=bf16_bits(wg))

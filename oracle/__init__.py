@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "orc_forward": (I, [P, P, P, P, I, I, I, I, I, F, P, P, P, P, P, P, P, P, P, P]),
             "orc_forward_tokens": (I, [P, P, P, P, I, I, I, I, I, F, P, I, P, P]),
             "orc_gemm_bf16": (I, [P, I, I, P, I, P, I, P, I, P, P]),
+            "orc_router_logits": (I, [P, I, I, P, I, P, P]),
             "orc_ffn_tokens": (I, [P, P, P, P, I, I, I, I, I, F, P, I, P, P]),
             "orc_swiglu_f32": (I, [P, I, I, P]),
             "orc_quant_rows_f32": (I, [P, I, I, P, P]),
@@ -269,6 +270,20 @@ def gemm_bf16(A, W, offsets, rows_list=None):
     _check(lib().orc_gemm_bf16(_p(A), rows, K, _p(W), N, _p(offsets), E, _p(rl),
                                0 if rl is None else n, _p(out), _p(out64)), "orc_gemm_bf16")
     return out, out64
+
+
+def router_logits(x_bf16, w_gate_bf16):
+    """Router projection: logits f32 [M][E] and their double sums for x [M][H], w_gate [E][H]
+    (both bf16 bits)."""
+    x = _c(x_bf16, np.uint16)
+    wg = _c(w_gate_bf16, np.uint16)
+    M, H = x.shape
+    E = wg.shape[0]
+    logits = np.zeros((M, E), np.float32)
+    logits64 = np.zeros((M, E), np.float64)
+    _check(lib().orc_router_logits(_p(x), M, H, _p(wg), E, _p(logits), _p(logits64)),
+           "orc_router_logits")
+    return logits, logits64
 
 
 def ffn_tokens(logits, x_bf16, w_up, w_down, k: int, cap: float, tokens=None):

@@ -437,6 +437,27 @@ int orc_gemm_bf16(const uint16_t* A, int rows, int K, const uint16_t* W, int N,
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* [WEAVE] section 3.1: the gate (router projection) counted in the layer's forward      */
+/* ------------------------------------------------------------------------------------ */
+
+/* logits[t][e] = fp32( sum_h x[t][h] * w_gate[e][h] ): bf16 operands, every product and the
+ * sum in double, one rounding to fp32 (logits64, optional, keeps the double sums). */
+int orc_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
+                      float* logits, double* logits64) {
+    if (!x || !w_gate || !logits || M < 0 || H < 1 || E < 1) return -1;
+    for (long t = 0; t < M; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += orc_bf16_value(x[t * H + h]) * orc_bf16_value(w_gate[(size_t)e * H + h]);
+            logits[t * E + e] = (float)acc;
+            if (logits64) logits64[t * E + e] = acc;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* [WEAVE] Mixtral-like layer: route, per-route expert FFN with SiLU gating, combine    */
 /* ------------------------------------------------------------------------------------ */
 

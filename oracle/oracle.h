@@ -103,6 +103,11 @@ int orc_forward_tokens(const float* logits, const uint16_t* x, const uint8_t* w_
                        const int32_t* tokens, int ntok, uint16_t* y, double* y64);
 
 /* ---- [H200] BF16 grouped GEMM (pure GEMM on compact expert rows) ------------------- */
+/* Router projection ([WEAVE] section 3.1 counts the gate in the layer): x bf16 [M][H],
+ * w_gate bf16 [E][H] -> logits f32 [M][E] = fp32(sum_h x*w in double); logits64 optional. */
+int orc_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
+                      float* logits, double* logits64);
+
 /* out[i][n] = bf16( sum_k A[r][k] * W[e(r)][n][k] ) for r = rows_list[i] (all rows when
  * rows_list is NULL); e(r) is the expert whose segment [offsets[e], offsets[e+1]) holds r. */
 int orc_gemm_bf16(const uint16_t* A, int rows, int K, const uint16_t* W, int N,
