@@ -250,6 +250,44 @@ def bench_ffn(args, moe, synth, torch, np):
     print(json.dumps(result))
 
 
+def bench_router(args, moe, synth, torch, np):
+    """--workload router_M<M>_H<H>_E<E>: the router projection (moe_router_logits) alone,
+    logits f32 [M,E] = x bf16 [M,H] . w_gate bf16 [E,H]^T; HBM-bound (x and w_gate read once)."""
+    _, ms, hs, es = args.workload.split("_")
+    M, H, E = int(ms[1:]), int(hs[1:]), int(es[1:])
+    d = synth.router_inputs(M, H, E, seed=0)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    wg = torch.from_numpy(d["w_gate"].view(np.int16)).to(dev)
+    out = torch.empty((M, E), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        moe.router_logits(x, wg, out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        moe.router_logits(x, wg, out)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+    nbytes = M * H * 2 + E * H * 2 + M * E * 4
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "µs per router projection + %HBM roofline",
+        "value": round(us, 3), "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate, fp32 out)",
+        "data": "synthetic", "config": {"workload": args.workload, "M": M, "H": H, "E": E},
+        "effective_tflops": round(2.0 * M * H * E / (us * 1e-6) / 1e12, 3),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "roofline": {"bound": "hbm", "kernel": "router_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}}))
+
+
 def bench_mlp(args, moe, synth, torch, np):
     """--workload mlp_fp8_M<M>_E<E>_k<k>_H<H>_I<I>: the whole FP8 expert MLP layer per step
     (route, layouts, QSG, gate+up FP8 GEMM, silu(g)*u requantise, down FP8 GEMM, combine);
@@ -444,6 +482,9 @@ def main():
         return
     if args.workload.startswith("mlp_fp8_"):
         bench_mlp(args, moe, synth, torch, np)
+        return
+    if args.workload.startswith("router_"):
+        bench_router(args, moe, synth, torch, np)
         return
     d = synth.workload_inputs(args.workload)
     M, E, k, K, N, cap = d["M"], d["E"], d["k"], d["K"], d["N"], d["cap"]

@@ -403,6 +403,16 @@ int moe_route(const float* logits, int M, int E, int k, float softcap, int32_t* 
                                    (hipStream_t)stream));
 }
 
+int moe_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
+                      float* logits, moe_stream_t stream) {
+    if (M < 0 || H < 64 || H % 64 || E < 1 || E > kMaxE || (long long)M * H >= (1LL << 40))
+        return MOE_E_INVAL;
+    if (M > 0 && (!x || !w_gate || !logits)) return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(launch_router_logits(x, M, H, w_gate, E, logits, (hipStream_t)stream));
+}
+
 int moe_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k, int K,
                        float softcap, int32_t* topk_ids, float* topk_weights, uint8_t* x_q,
                        float* x_scales, moe_stream_t stream) {

@@ -15,6 +15,10 @@ struct DeviceInfo {
 };
 const DeviceInfo& device_info();
 
+// logits f32 [M][E] = x bf16 [M][H] . w_gate bf16 [E][H]^T (H a multiple of 64)
+hipError_t launch_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
+                                float* logits, hipStream_t s);
+
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
                         int32_t* ids, float* weights, hipStream_t s);
 // the same, with zero0[0..zero_n) and zero1[0..zero_n) cleared by its first workgroup

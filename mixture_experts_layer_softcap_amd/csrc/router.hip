@@ -1,0 +1,131 @@
+// router.hip -- the router projection ahead of the route ([WEAVE] section 3.1 counts the gate
+// in the layer's forward): logits[t][e] = sum_h x[t][h] * w_gate[e][h], bf16 operands, fp32
+// accumulate, fp32 logits.
+//
+// The operation is a skinny GEMM (E = 8..1024 columns) that is bound by reading x and w_gate,
+// so it runs straight from global memory without LDS staging: per 64-wide k step a lane loads
+// 2 x 16 bytes of one gate row and 2 x 16 bytes of one token row (each row's 128 bytes read
+// by 4 lanes, whole cache lines), and feeds two v_mfma_f32_16x16x32_bf16 with gate rows as
+// the 16-row A side and tokens as the B side, so a lane ends with 4 consecutive logits of one
+// token.  A workgroup owns 16 tokens x 16*EB experts; its 4 waves split K in contiguous
+// quarters and sum their fp32 partials through LDS in wave order, so the result does not
+// depend on timing.  Token rows past M and gate rows past E repeat the last row and are not
+// stored.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRing = 4;                      // 64-wide k steps in flight per wave
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int EB>
+__global__ __launch_bounds__(kWaves * 64) void router_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wg,
+                                                             int M, int H, int E,
+                                                             float* __restrict__ logits) {
+    __shared__ v4f s_part[kWaves - 1][EB][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * 16;
+    const int e0 = blockIdx.y * 16 * EB;
+    const int nsteps = H >> 6;
+    const int s0 = nsteps * wave / kWaves, s1 = nsteps * (wave + 1) / kWaves;
+
+    // this lane's rows: token t0 + j (B side) and gate rows e0 + 16b + j (A side), bytes
+    // [16g, 16g+16) and [64+16g, 64+16g+16) of every 128-byte k step
+    const uint16_t* xr = x + (size_t)min(t0 + j, M - 1) * H + g * 8;
+    const uint16_t* wr[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b) wr[b] = wg + (size_t)min(e0 + 16 * b + j, E - 1) * H + g * 8;
+
+    v4f acc[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b) acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    struct Unit {
+        uint4 x0, x1, w0[EB], w1[EB];
+    };
+    Unit ring[kRing];
+    auto load = [&](Unit& u, int s) __attribute__((always_inline)) {
+        const int k = s * 64;
+        u.x0 = *reinterpret_cast<const uint4*>(xr + k);
+        u.x1 = *reinterpret_cast<const uint4*>(xr + k + 32);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+            u.w0[b] = *reinterpret_cast<const uint4*>(wr[b] + k);
+            u.w1[b] = *reinterpret_cast<const uint4*>(wr[b] + k + 32);
+        }
+    };
+    // (loads past s1 repeat the last step so every lane issues the same loads; never used)
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) load(ring[i], min(s0 + i, max(s1 - 1, s0)));
+    for (int s = s0; s < s1; s += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) {
+            if (s + i < s1) {
+                const Unit u = ring[i];
+#pragma unroll
+                for (int b = 0; b < EB; ++b) {
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(u.w0[b]), as_bf16x8(u.x0), acc[b], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(u.w1[b]), as_bf16x8(u.x1), acc[b], 0, 0, 0);
+                }
+                load(ring[i], min(s + i + kRing, s1 - 1));
+            }
+        }
+    }
+
+    // partials of waves 1..3 to LDS; wave 0 adds them in wave order and stores
+    if (wave > 0) {
+#pragma unroll
+        for (int b = 0; b < EB; ++b) s_part[wave - 1][b][lane] = acc[b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+        v4f v = acc[b];
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w) v += s_part[w][b][lane];
+        // C layout of the 16x16 MFMA: lane (j, g) holds rows 4g..4g+3 (gate rows, i.e.
+        // experts) of column j (token)
+        const int t = t0 + j, e = e0 + 16 * b + 4 * g;
+        if (t < M && e < E) {
+            float* o = logits + (size_t)t * E + e;
+            if (e + 3 < E && (E & 3) == 0) {
+                *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (e + i < E) o[i] = v[i];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
+                                float* logits, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const unsigned tb = (unsigned)((M + 15) / 16);
+    // wider expert blocks (x fragments reused across them) once the grid covers the chip
+    const long long cus = device_info().cu_count;
+    if ((long long)tb * ((E + 63) / 64) >= 2 * cus) {
+        hipLaunchKernelGGL(router_kernel<4>, dim3(tb, (E + 63) / 64), dim3(kWaves * 64), 0, s, x,
+                           w_gate, M, H, E, logits);
+    } else {
+        hipLaunchKernelGGL(router_kernel<1>, dim3(tb, (E + 15) / 16), dim3(kWaves * 64), 0, s, x,
+                           w_gate, M, H, E, logits);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

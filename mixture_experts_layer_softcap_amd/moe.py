@@ -47,6 +47,7 @@ _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_device_check": (_I, []),
+    "moe_router_logits": (_I, [_P, _I, _I, _P, _I, _P, _P]),
     "moe_route": (_I, [_P, _I, _I, _I, _F, _P, _P, _P]),
     "moe_route_quantize": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "moe_max_tasks": (_I, [_I, _I, _I, _I, _I]),
@@ -245,6 +246,13 @@ def forward(logits, x, w_q, w_scales, k: int, softcap: float, out, workspace,
     _call("moe_forward_ex", _ptr(logits), _ptr(x), _ptr(w_q), _ptr(w_scales), M, E, k, K, N,
           softcap, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
           chunk_rows, flags, _stream(stream))
+
+
+def router_logits(x, w_gate, logits, stream=None):
+    """logits f32 [M][E] = x bf16 [M][H] . w_gate bf16 [E][H]^T (moe_router_logits)."""
+    M, H = x.shape
+    E = w_gate.shape[0]
+    _call("moe_router_logits", _ptr(x), M, H, _ptr(w_gate), E, _ptr(logits), _stream(stream))
 
 
 def forward_noalloc(logits, x, w_q, w_scales, k: int, softcap: float, out, stream=None):

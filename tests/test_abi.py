@@ -182,3 +182,14 @@ def test_forward_noalloc_rejects_on_the_host(L):
     assert na(P, P, NULL, P, 8, 16, 2, 256, 256, 30.0, P, S) == INVAL    # null weights
     assert na(P, P, P, P, 8, 16, 2, 256, 256, 30.0, NULL, S) == INVAL    # null out
     assert na(P, P, P, P, 8, 16, 2, 256, 256, float("nan"), P, S) == INVAL
+
+
+def test_router_logits_rejects_on_the_host(L):
+    INVAL = moe.MOE_E_INVAL
+    rl = L.moe_router_logits
+    assert rl(P, 8, 100, P, 4, P, S) == INVAL          # H % 64
+    assert rl(P, 8, 128, P, 0, P, S) == INVAL          # E = 0
+    assert rl(P, 8, 128, P, 1025, P, S) == INVAL       # E > 1024
+    assert rl(NULL, 8, 128, P, 4, P, S) == INVAL       # null x
+    assert rl(P, 8, 128, P, 4, NULL, S) == INVAL       # null logits
+    assert rl(P, -1, 128, P, 4, P, S) == INVAL
