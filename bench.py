@@ -515,8 +515,19 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- whole-step timing: events around every graph replay ---------------------------
+    # ---- whole-step timing: K back-to-back steps between two events (the value), then K
+    # more with an event after every step for the spread (an event between steps adds its
+    # own marker to the stream, so the second pass is not the value) ----------------------
     stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    us_layer = total_ms * 1e3 / args.steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     evs[0].record(stream)
@@ -525,8 +536,7 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]   # us
-    total_ms = evs[0].elapsed_time(evs[-1])
-    us_layer = total_ms * 1e3 / args.steps
+    us_evented = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
 
     # routing statistics of this input (its routed ids read back, outside timing)
     off = moe.forward_workspace_offset(M, E, k, K, N, 0)
@@ -626,6 +636,7 @@ def main():
                    "chunk_rows": chunk, "sched": args.sched if gather else None},
         "effective_tflops": round(flops / (us_layer * 1e-6) / 1e12, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "us_with_event_per_step": round(us_evented, 3),
         "layer_hbm_frac": round(lbytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_algorithmic_bytes": lbytes,
         "nonempty_experts": int((counts > 0).sum()),
