@@ -44,6 +44,9 @@ def parse():
                    help="task schedule of the LDS-tiled grouped GEMMs: hardware dispatch of one "
                         "workgroup per task, a static persistent walk, one atomic queue, or "
                         "per-XCD atomic queues (auto: the library's default)")
+    p.add_argument("--atomic-combine", action="store_true",
+                   help="gathering path: the scatter-add combine (fp32 atomics into token rows, "
+                        "then bf16) instead of fp32 routed rows and a gather-sum kernel")
     p.add_argument("--graph", action="store_true",
                    help="replay the cached HIP graph of the step instead of launching its kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -505,7 +508,8 @@ def main():
     sched = SCHEDS[args.sched]
     flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
         (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0) | \
-        (moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0)
+        (moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0) | \
+        (moe.MOE_FWD_ATOMIC_COMBINE if args.atomic_combine else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,

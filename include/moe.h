@@ -304,6 +304,13 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  * 0 picks the default.  The queue forms use workspace part 7 as their counters. */
 #define MOE_FWD_SCHED(s) (((s) + 1) << 3)
 #define MOE_FWD_SCHED_MASK (7 << 3)
+/* bit 6: the combine as the pages' scatter-add ([FMF8] Fusion 1): the gathering GEMM adds
+ * w_tj * h of every routed row into fp32 token rows [M][N] (part 11, zeroed by the route
+ * kernel) with float atomics, and a last kernel rounds them to bf16.  The fp32 sums then
+ * follow atomic arrival order, so repeat calls may differ in the last bf16 bit.  Valid only on
+ * the gathering path (chunk_rows in [65, 256], K <= 8192, not STAGED) with hardware
+ * dispatch. */
+#define MOE_FWD_ATOMIC_COMBINE 64
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,

@@ -134,7 +134,7 @@ struct FwdArgs {
 };
 
 constexpr int kFwdFlagBits = MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED |
-                             MOE_FWD_SCHED_MASK;
+                             MOE_FWD_SCHED_MASK | MOE_FWD_ATOMIC_COMBINE;
 bool fwd_flags_ok(int flags) {
     return !(flags & ~kFwdFlagBits) && ((flags & MOE_FWD_SCHED_MASK) >> 3) <= 4;
 }
@@ -174,13 +174,25 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         uint8_t* x_q = reinterpret_cast<uint8_t*>(at(13));
         float* x_s = reinterpret_cast<float*>(at(14));
         int32_t* rel = reinterpret_cast<int32_t*>(at(15));
+        // the scatter-add form accumulates into fp32 token rows [M][N] (in the rows' space),
+        // zeroed by the route kernel
+        const bool atomic = a.flags & MOE_FWD_ATOMIC_COMBINE;
         if ((e = launch_route_quantize_zero(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids,
-                                            wts, x_q, x_s, counts, rel, a.E, s)) != hipSuccess)
+                                            wts, x_q, x_s, counts, rel, a.E, s,
+                                            atomic ? rows : nullptr, a.N)) != hipSuccess)
             return e;
         if ((e = launch_layout_sorted_wide(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets,
                                            cursors, tasks, ntasks, queue, rel, sorted, s)) !=
             hipSuccess)
             return e;
+        if (atomic) {
+            if ((e = launch_gemm_fp8_tile_gather_atomic(x_q, x_s, a.M, a.k, a.K, a.w_q,
+                                                        a.w_scales, a.N, tasks, ntasks,
+                                                        max_tasks, a.chunk, sorted, wts, rows,
+                                                        s)) != hipSuccess)
+                return e;
+            return launch_acc_to_bf16(rows, a.M, a.N, a.out, s);
+        }
         if ((e = launch_gemm_fp8_tile_gather(x_q, x_s, a.M, a.k, a.K, a.w_q, a.w_scales, a.N,
                                              tasks, ntasks, max_tasks, a.chunk, sorted, rows,
                                              fwd_sched(a.flags, a.chunk), queue, s)) !=
@@ -608,6 +620,10 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
     const int sched = ((flags & MOE_FWD_SCHED_MASK) >> 3) - 1;
     if (sched > MOE_SCHED_DISPATCH && chunk > 128) return MOE_E_INVAL;
+    // the scatter-add form exists for the gathering tiled path under hardware dispatch
+    if ((flags & MOE_FWD_ATOMIC_COMBINE) &&
+        ((flags & MOE_FWD_STAGED) || !gemm_fp8_tile_applies(K, chunk) || sched > 0))
+        return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;
     FwdArgs a{logits, x, w_q, w_scales, M, E, k, K, N, softcap, out, workspace, chunk, flags};

@@ -51,6 +51,11 @@ constexpr int kMaxKB = 64;                    // K <= 8192
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Epilogue of the pages' scatter-add form (internal; gathering launches only): every routed
+// row h of route r (token r / kr) is added as w[r] * h into the fp32 accumulator rows `out`
+// [M][N] with float atomics.
+constexpr int kEpiAtomicAdd = 100;
+
 template <int BM>
 struct TileCfg {
     static constexpr int kStages = BM == 128 ? 3 : 2;
@@ -112,7 +117,7 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
                           const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                           const int32_t* __restrict__ sorted_route_ids, void* __restrict__ out,
                           int rows, int K, int N, int pairs, int cus_x, int kr,
-                          uint32_t* __restrict__ queue) {
+                          uint32_t* __restrict__ queue, const float* __restrict__ topk_weights) {
     using Cfg = TileCfg<BM>;
     constexpr int S = Cfg::kStages;
     constexpr bool PERSIST = SCHED != MOE_SCHED_DISPATCH;
@@ -284,12 +289,19 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
                 const int m = r * 16 + j;
                 if (r >= nrg || m >= rc) continue;
                 size_t row = (size_t)(rb + m);
-                if (EPI == MOE_EPI_ROUTE_F32) row = (size_t)sorted_route_ids[rb + m];
+                if (EPI == MOE_EPI_ROUTE_F32 || EPI == kEpiAtomicAdd)
+                    row = (size_t)sorted_route_ids[rb + m];
+                float wv = 0.0f;
+                if constexpr (EPI == kEpiAtomicAdd) wv = topk_weights[row];
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     const int n = nb0 * 128 + wave * 32 + b * 16 + g * 4;
                     const v4f c = acc[b][r];
-                    if (EPI == MOE_EPI_STORE_BF16) {
+                    if constexpr (EPI == kEpiAtomicAdd) {
+                        float* dst = static_cast<float*>(out) + (row / kr) * N + n;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, wv * c[i]);
+                    } else if (EPI == MOE_EPI_STORE_BF16) {
                         uint2 v;
                         v.x = f32_to_bf16(c[0]) | (f32_to_bf16(c[1]) << 16);
                         v.y = f32_to_bf16(c[2]) | (f32_to_bf16(c[3]) << 16);
@@ -399,14 +411,15 @@ template <int BM, int EPI, int KBC, bool GATHER, int SCHED>
 hipError_t launch_tile(const uint8_t* a, const float* a_scales, int rows, int K,
                        const uint8_t* w, const float* w_scales, int N, const moe_task* tasks,
                        const int32_t* ntasks, int max_tasks, const int32_t* sorted, void* out,
-                       int kr, uint32_t* queue, hipStream_t s) {
+                       int kr, uint32_t* queue, hipStream_t s,
+                       const float* topk_weights = nullptr) {
     const int Nb = N / 128;
     const int pairs = (Nb + 1) / 2;
     const int cus_x = max(2, device_info().cu_count / 8);
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<BM, EPI, KBC, GATHER, SCHED>),
                        dim3(tile_grid(SCHED, N, max_tasks)), dim3(kThreads), 0, s, a, a_scales, w,
                        w_scales, reinterpret_cast<const int4*>(tasks), ntasks, sorted, out, rows,
-                       K, N, pairs, cus_x, kr, queue);
+                       K, N, pairs, cus_x, kr, queue, topk_weights);
     return hipGetLastError();
 }
 

@@ -65,4 +65,25 @@ hipError_t launch_gemm_fp8_tile_gather(const uint8_t* x_q, const float* x_scales
                                 max_tasks, sorted, rows_out, queue, s);
 }
 
+hipError_t launch_gemm_fp8_tile_gather_atomic(const uint8_t* x_q, const float* x_scales, int M,
+                                              int k, int K, const uint8_t* w,
+                                              const float* w_scales, int N,
+                                              const moe_task* tasks, const int32_t* ntasks,
+                                              int max_tasks, int chunk_rows,
+                                              const int32_t* sorted, const float* weights,
+                                              float* acc, hipStream_t s) {
+    if (max_tasks <= 0) return hipSuccess;
+#define MOE_TILE_ARGS x_q, x_scales, M, K, w, w_scales, N, tasks, ntasks, max_tasks, sorted, acc, \
+                      k, nullptr, s, weights
+    if (chunk_rows <= 128) {
+        if (K == 2048)
+            return launch_tile<128, kEpiAtomicAdd, 16, true, MOE_SCHED_DISPATCH>(MOE_TILE_ARGS);
+        return launch_tile<128, kEpiAtomicAdd, 0, true, MOE_SCHED_DISPATCH>(MOE_TILE_ARGS);
+    }
+    if (K == 2048)
+        return launch_tile<256, kEpiAtomicAdd, 16, true, MOE_SCHED_DISPATCH>(MOE_TILE_ARGS);
+    return launch_tile<256, kEpiAtomicAdd, 0, true, MOE_SCHED_DISPATCH>(MOE_TILE_ARGS);
+#undef MOE_TILE_ARGS
+}
+
 }  // namespace moe

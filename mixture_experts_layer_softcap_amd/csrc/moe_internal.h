@@ -32,10 +32,12 @@ hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, 
                                  uint8_t* x_q, float* x_scales, hipStream_t s);
 
 // the same, also zeroing zero0[0..zero_n) and zero1[0..zero_n) (scratch of the wide layout)
+// and, with acc != nullptr, the fp32 accumulator rows acc [M][acc_n] (acc_n % 4 == 0)
 hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
                                       int k, int K, float softcap, int32_t* ids, float* weights,
                                       uint8_t* x_q, float* x_scales, int32_t* zero0,
-                                      int32_t* zero1, int zero_n, hipStream_t s);
+                                      int32_t* zero1, int zero_n, hipStream_t s,
+                                      float* acc = nullptr, int acc_n = 0);
 
 // the layout with the sorted route ids over many workgroups: counts and rel [E] must be zero;
 // optionally route -> slot and a second task list over the same chunks (n_blocks2 panels)
@@ -103,6 +105,17 @@ hipError_t launch_gemm_fp8_tile_gather(const uint8_t* x_q, const float* x_scales
                                        int max_tasks, int chunk_rows, const int32_t* sorted,
                                        float* rows_out, int sched, uint32_t* queue,
                                        hipStream_t s);
+// the same GEMM with the scatter-add epilogue of the pages: every routed row h is added as
+// w[r] * h into acc [M][N] (fp32 atomics; acc zeroed beforehand), hardware dispatch
+hipError_t launch_gemm_fp8_tile_gather_atomic(const uint8_t* x_q, const float* x_scales, int M,
+                                              int k, int K, const uint8_t* w,
+                                              const float* w_scales, int N,
+                                              const moe_task* tasks, const int32_t* ntasks,
+                                              int max_tasks, int chunk_rows,
+                                              const int32_t* sorted, const float* weights,
+                                              float* acc, hipStream_t s);
+// out bf16 [M][N] = bf16(acc) (round to nearest even)
+hipError_t launch_acc_to_bf16(const float* acc, int M, int N, uint16_t* out, hipStream_t s);
 
 // small-batch forward GEMM with the layout, sort/gather and quantisation folded in: weight
 // slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])

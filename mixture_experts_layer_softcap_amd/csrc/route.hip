@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, float softcap,
     int32_t* __restrict__ ids, float* __restrict__ weights, const uint16_t* __restrict__ x,
     int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales, int32_t* __restrict__ zero0,
-    int32_t* __restrict__ zero1, int zero_n) {
+    int32_t* __restrict__ zero1, int zero_n, float* __restrict__ acc, int acc_n) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (QUANT && blockIdx.y > 0) {
@@ -61,6 +61,12 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         // values per pass: lane l holds values [8l, 8l+8) of the pass, so a 128-value block
         // is an aligned group of 16 lanes, wholly inside or outside the slice
         if (t >= M) return;
+        if (acc && blockIdx.y == 1) {
+            // the token's fp32 accumulator row that the grouped GEMM adds its routes into
+            for (int n = lane * 4; n < acc_n; n += 256)
+                *reinterpret_cast<float4*>(acc + (size_t)t * acc_n + n) =
+                    make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         const int per = (K / 128 + kQuantSplit - 1) / kQuantSplit * 128;
         const int k_lo = (blockIdx.y - 1) * per;
         const int k_hi = min(K, k_lo + per);
@@ -153,26 +159,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                       float* weights, const uint16_t* x, int K, uint8_t* x_q, float* x_scales,
-                      int32_t* z0, int32_t* z1, int zn, hipStream_t s) {
+                      int32_t* z0, int32_t* z1, int zn, float* acc, int acc_n, hipStream_t s) {
     const int per = M >= kRouteWaves * device_info().cu_count ? kRouteWaves : 1;
     const int grid = (M + per - 1) / per;
     if (x_q)
         hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid, 1 + kQuantSplit),
-                           dim3(64 * per), 0, s, logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
-                           z1, zn);
+                           dim3(64 * per), 0, s, logits, M, E, k, softcap, ids, weights, x, K, x_q,
+                           x_scales, z0, z1, zn, acc, acc_n);
     else
         hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * per), 0, s,
                            logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
-                           z1, zn);
+                           z1, zn, acc, acc_n);
     return hipGetLastError();
 }
 
 hipError_t launch_route_any(const float* logits, int M, int E, int k, float softcap,
                             int32_t* ids, float* weights, const uint16_t* x, int K,
                             uint8_t* x_q, float* x_scales, int32_t* z0, int32_t* z1, int zn,
-                            hipStream_t s) {
+                            hipStream_t s, float* acc = nullptr, int acc_n = 0) {
     if (M == 0) return hipSuccess;
-#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0, z1, zn, s
+#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0, z1, zn, \
+                       acc, acc_n, s
     if (E <= 64) return launch_vpl<1>(MOE_ROUTE_ARGS);
     if (E <= 128) return launch_vpl<2>(MOE_ROUTE_ARGS);
     if (E <= 256) return launch_vpl<4>(MOE_ROUTE_ARGS);
@@ -206,9 +213,10 @@ hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, 
 hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
                                       int k, int K, float softcap, int32_t* ids, float* weights,
                                       uint8_t* x_q, float* x_scales, int32_t* zero0,
-                                      int32_t* zero1, int zero_n, hipStream_t s) {
+                                      int32_t* zero1, int zero_n, hipStream_t s, float* acc,
+                                      int acc_n) {
     return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, zero0,
-                            zero1, zero_n, s);
+                            zero1, zero_n, s, acc, acc_n);
 }
 
 }  // namespace moe

@@ -113,4 +113,32 @@ hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const f
     return launch_slots<false>(rows, route_slots, weights, ids, M, k, E, N, out, s);
 }
 
+namespace {
+
+// out[i] = bf16(acc[i]) for the accumulator rows of the scatter-add form, 8 per thread
+__global__ __launch_bounds__(kThreads) void acc_to_bf16_kernel(const float* __restrict__ acc,
+                                                               size_t n8,
+                                                               uint16_t* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n8) return;
+    const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
+    uint4 o;
+    o.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+    o.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+    o.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
+    o.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+    reinterpret_cast<uint4*>(out)[i] = o;
+}
+
+}  // namespace
+
+hipError_t launch_acc_to_bf16(const float* acc, int M, int N, uint16_t* out, hipStream_t s) {
+    const size_t n8 = (size_t)M * N / 8;        // N a multiple of 128
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(acc_to_bf16_kernel, dim3((unsigned)((n8 + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, acc, n8, out);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -30,6 +30,7 @@ MOE_EPI_SWIGLU_BF16 = 3
 MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
 MOE_FWD_STAGED = 4
+MOE_FWD_ATOMIC_COMBINE = 64
 
 MOE_QUEUE_WORDS = 16
 MOE_SCHED_AUTO = -1

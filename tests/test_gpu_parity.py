@@ -15,7 +15,8 @@ import torch
 import oracle as orc
 from mixture_experts_layer_softcap_amd import moe, synth
 
-from gpu_util import (DEV, WEIGHT_RTOL, assert_bf16_close, assert_gemm_f32_close,
+from gpu_util import (DEV, WEIGHT_RTOL, assert_bf16_close, assert_gemm_f32_close, bf16_f64,
+                      bf16_ulp,
                       canonical_segments, oracle_gemm_rows_by_expert, oracle_rows_parallel,
                       oracle_threads, to_dev, to_np, workload, zeros)
 
@@ -807,6 +808,31 @@ def test_forward_skewed_schedules(name):
             assert_bf16_close(base, ref["y64"], f"{name} sched={s}")
         for o in outs:
             np.testing.assert_array_equal(o, base)
+
+
+@pytest.mark.parametrize("chunk", [0, 256])
+@pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
+def test_forward_skewed_atomic_combine(name, chunk):
+    # the pages' scatter-add combine (fp32 atomics into token rows, then bf16): the whole
+    # output against the oracle; the fp32 sums follow arrival order, so repeats may differ in
+    # the last bit but stay within the bar; repeated calls reuse the accumulator rows
+    d = workload(name)
+    ref = skewed_reference(name)
+    outs = gpu_forward(d, reps=3, chunk=chunk, flags=moe.MOE_FWD_ATOMIC_COMBINE)
+    for o in outs:
+        assert_bf16_close(o, ref["y64"], f"{name} atomic combine chunk={chunk}")
+    # against the gather-sum: one bf16 step, plus the fp32 summation-order difference near
+    # zero (k terms of magnitude ~rms in either order differ by a few fp32 ulps of rms)
+    plain = bf16_f64(gpu_forward(d, chunk=chunk)[0])
+    rms = float(np.sqrt(np.mean(plain ** 2)))
+    diff = np.abs(bf16_f64(outs[0]) - plain)
+    assert (diff <= bf16_ulp(plain) + 2.0 ** -18 * rms).all()
+
+
+def test_forward_atomic_combine_only_on_the_gathering_path():
+    d = workload(QWEN)                               # the small-batch path
+    with pytest.raises(moe.MoeError):
+        gpu_forward(d, flags=moe.MOE_FWD_ATOMIC_COMBINE)
 
 
 @pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
