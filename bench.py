@@ -108,6 +108,18 @@ def layer_algorithmic_bytes(counts, M, E, k, K, N):
     return nonempty * (N * K + (N // 128) * (K // 128) * 4) + M * E * 4 + M * K * 2 + M * N * 2
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, k, cap, budget_s=12.0):
     import oracle
 
@@ -121,6 +133,7 @@ def cpu_baseline(d, k, cap, budget_s=12.0):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": med * 1e6, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"whole layer ({d['M']} tokens, fp64 single-threaded C oracle), "
                       f"median of {len(times)} runs; host has {os.cpu_count()} cores"}
 
@@ -248,7 +261,8 @@ def bench_ffn(args, moe, synth, torch, np):
         "roofline": {"bound": "mfma", "kernel": "whole layer (gemm_bf16_kernel x2 + glue)",
                      "achieved": round(tflops, 2), "peak": BF16_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_launch_us": round(us, 3)},
+                     "traffic": measured_traffic(args.workload, "whole layer"),
+                     "avg_launch_us": round(us, 3)},
     }
     print(json.dumps(result))
 
@@ -266,7 +280,31 @@ def bench_router(args, moe, synth, torch, np):
     for _ in range(args.warmup):
         moe.router_logits(x, wg, out)
     torch.cuda.synchronize()
+    eager = out.clone()
+    # one call is a few microseconds of GPU work, less than a ctypes call costs on the host, so
+    # the timed steps are one captured graph of K back-to-back calls (the kernel launches only;
+    # the projection allocates and clears nothing), replayed once warm and once timed
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(args.steps):
+                moe.router_logits(x, wg, out)
+    torch.cuda.current_stream().wait_stream(cs)
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager):
+        raise SystemExit("router graph replay differs from the eager call")
     stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # plain launches from Python, for the host-bound figure
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     evs[0].record(stream)
     for i in range(args.steps):
@@ -274,7 +312,7 @@ def bench_router(args, moe, synth, torch, np):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
-    us = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
+    us_plain = evs[0].elapsed_time(evs[-1]) * 1e3 / args.steps
     nbytes = M * H * 2 + E * H * 2 + M * E * 4
     achieved = nbytes / (us * 1e-6) / 1e9
     print(json.dumps({
@@ -284,10 +322,13 @@ def bench_router(args, moe, synth, torch, np):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate, fp32 out)",
         "data": "synthetic", "config": {"workload": args.workload, "M": M, "H": H, "E": E},
         "effective_tflops": round(2.0 * M * H * E / (us * 1e-6) / 1e12, 3),
-        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
+        "timing": "one graph of K back-to-back calls",
+        "us_per_call_plain_launches": round(us_plain, 3),
+        "plain_us_p10_p50_p90": [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)],
         "roofline": {"bound": "hbm", "kernel": "router_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "router_kernel"),
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}}))
 
 
@@ -425,7 +466,7 @@ def bench_mlp(args, moe, synth, torch, np):
             times.append(time.perf_counter() - t0)
         result["cpu_baseline"] = {
             "value": statistics.median(times) * 1e6, "unit": "us/layer", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"whole layer ({M} tokens, fp64 single-threaded C oracle), median of "
                       f"{len(times)} runs; host has {os.cpu_count()} cores"}
     print(json.dumps(result))

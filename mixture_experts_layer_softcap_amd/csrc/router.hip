@@ -33,8 +33,18 @@ __global__ __launch_bounds__(kWaves * 64) void router_kernel(const uint16_t* __r
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.x * 16;
-    const int e0 = blockIdx.y * 16 * EB;
+    // workgroup i runs on XCD i % 8 (round-robin dispatch); when the expert blocks divide
+    // evenly over the 8 XCDs, all token blocks of one expert block go to the same XCD, so its
+    // gate rows come from HBM once and are re-read from that XCD's L2
+    const int ntb = (M + 15) >> 4, neb = gridDim.x / ntb;
+    int tb = blockIdx.x % ntb, eb = blockIdx.x / ntb;
+    if ((neb & 7) == 0) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        tb = slot % ntb;
+        eb = xcd + 8 * (slot / ntb);
+    }
+    const int t0 = tb * 16;
+    const int e0 = eb * 16 * EB;
     const int nsteps = H >> 6;
     const int s0 = nsteps * wave / kWaves, s1 = nsteps * (wave + 1) / kWaves;
 
@@ -119,11 +129,11 @@ hipError_t launch_router_logits(const uint16_t* x, int M, int H, const uint16_t*
     // wider expert blocks (x fragments reused across them) once the grid covers the chip
     const long long cus = device_info().cu_count;
     if ((long long)tb * ((E + 63) / 64) >= 2 * cus) {
-        hipLaunchKernelGGL(router_kernel<4>, dim3(tb, (E + 63) / 64), dim3(kWaves * 64), 0, s, x,
-                           w_gate, M, H, E, logits);
+        hipLaunchKernelGGL(router_kernel<4>, dim3(tb * ((E + 63) / 64)), dim3(kWaves * 64), 0, s,
+                           x, w_gate, M, H, E, logits);
     } else {
-        hipLaunchKernelGGL(router_kernel<1>, dim3(tb, (E + 15) / 16), dim3(kWaves * 64), 0, s, x,
-                           w_gate, M, H, E, logits);
+        hipLaunchKernelGGL(router_kernel<1>, dim3(tb * ((E + 15) / 16)), dim3(kWaves * 64), 0, s,
+                           x, w_gate, M, H, E, logits);
     }
     return hipGetLastError();
 }
