@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--atomic-combine", action="store_true",
                    help="gathering path: the scatter-add combine (fp32 atomics into token rows, "
                         "then bf16) instead of fp32 routed rows and a gather-sum kernel")
+    p.add_argument("--fused-route", action="store_true",
+                   help="small-batch path: the route inside the grouped GEMM (two kernels)")
     p.add_argument("--graph", action="store_true",
                    help="replay the cached HIP graph of the step instead of launching its kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -550,7 +552,8 @@ def main():
     flags = (moe.MOE_FWD_STATIC_GRID if args.static_grid else 0) | \
         (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0) | \
         (moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0) | \
-        (moe.MOE_FWD_ATOMIC_COMBINE if args.atomic_combine else 0)
+        (moe.MOE_FWD_ATOMIC_COMBINE if args.atomic_combine else 0) | \
+        (moe.MOE_FWD_FUSED_ROUTE if args.fused_route else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -596,7 +599,7 @@ def main():
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if K <= 8192 else 64))
     nkern = moe.forward_kernels(M, E, k, K, N, args.chunk_rows, flags)
-    fused = nkern == 3
+    fused = nkern in (2, 3)
     gather = not args.staged and 64 < chunk <= 256 and K <= 8192
     rows_out = torch.empty((R, N), dtype=torch.float32, device=dev)
     if gather:
@@ -667,7 +670,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "K": K, "N": N,
                    "softcap": cap, "weight_copies_rotated": copies,
-                   "path": ("3 kernels: route, grouped GEMM from the routed ids, combine" if fused
+                   "path": ("2 kernels: grouped GEMM routing its tokens itself, combine"
+                            if nkern == 2
+                            else "3 kernels: route, grouped GEMM from the routed ids, combine"
+                            if fused
                             else "5 kernels: route+quantise, count, sort+layout, gathering "
                                  "grouped GEMM, combine" if gather
                             else "5 kernels: route, layout, QSG, grouped GEMM, combine"),

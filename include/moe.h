@@ -50,6 +50,11 @@ typedef void* moe_stream_t; /* hipStream_t */
 /* Words of a grouped-GEMM task-counter buffer (`queue` arguments): per-XCD tickets, an exit
  * count and an error word.  Zero before first use; every launch leaves it zeroed. */
 #define MOE_QUEUE_WORDS 16
+/* Word of moe_forward's part 7 (the task counters) that the step sets to 1 when the
+ * route-fused GEMM (MOE_FWD_FUSED_ROUTE) stopped waiting for the routed ids: that step's
+ * output is then not valid.  It stays set until the caller clears it or a step that builds a
+ * layout resets the counters. */
+#define MOE_QUEUE_HANDOFF_STATUS 10
 
 /* Task schedules of the LDS-tiled grouped GEMMs (BF16, and FP8 with chunks of 65..256 rows)
  * ([WEAVE] sections 1.2, 2.2, 3.1 and 4.2):
@@ -311,13 +316,22 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  * the gathering path (chunk_rows in [65, 256], K <= 8192, not STAGED) with hardware
  * dispatch. */
 #define MOE_FWD_ATOMIC_COMBINE 64
+/* bit 7: on the small-batch path with E <= 256 and at most 8 tokens per CU, run two kernels
+ * instead of three: the route moves into the grouped GEMM ([FMF8] "Baseline: 7 kernels"
+ * item 1 fused with items 2-6).  Token t is routed by one wave of workgroup t % CUs, which
+ * writes topk_ids and topk_weights and publishes each route as a tagged word in part 12
+ * (route_slots, unused on this path); every workgroup waits for the route words it reads (a
+ * bounded wait, see MOE_QUEUE_HANDOFF_STATUS) and the combine clears them.  Same results as
+ * without the bit.  Elsewhere the bit is ignored. */
+#define MOE_FWD_FUSED_ROUTE 128
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
 
-/* Number of kernels moe_forward_ex launches for these arguments: 3 (small batch) or 5 (the
- * gathering path or the staged one); MOE_E_INVAL for arguments moe_forward_ex rejects. */
+/* Number of kernels moe_forward_ex launches for these arguments: 2 (small batch with
+ * MOE_FWD_FUSED_ROUTE), 3 (small batch) or 5 (the gathering path or the staged one);
+ * MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
 /* ---- the whole step for callers that cannot allocate ----------------------------------

@@ -134,7 +134,14 @@ struct FwdArgs {
 };
 
 constexpr int kFwdFlagBits = MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED |
-                             MOE_FWD_SCHED_MASK | MOE_FWD_ATOMIC_COMBINE;
+                             MOE_FWD_SCHED_MASK | MOE_FWD_ATOMIC_COMBINE | MOE_FWD_FUSED_ROUTE;
+
+// Whether the step runs as two kernels: the small-batch GEMM with the route inside, then the
+// combine.
+bool fwd_route_fused(int M, int E, int k, int K, int N, int chunk, int flags) {
+    return (flags & MOE_FWD_FUSED_ROUTE) && !(flags & MOE_FWD_STAGED) &&
+           forward_fused_applies(M, k, E, K, N, chunk) && fused_route_applies(M, k, E);
+}
 bool fwd_flags_ok(int flags) {
     return !(flags & ~kFwdFlagBits) && ((flags & MOE_FWD_SCHED_MASK) >> 3) <= 4;
 }
@@ -199,6 +206,18 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
             hipSuccess)
             return e;
         return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
+    }
+    if (fwd_route_fused(a.M, a.E, a.k, a.K, a.N, a.chunk, a.flags)) {
+        // two kernels: the route runs inside the GEMM, handing the routes over through tagged
+        // words in the otherwise unused route_slots part; the combine clears them again
+        uint32_t* handoff = reinterpret_cast<uint32_t*>(slots);
+        if ((e = launch_gemm_fp8_fused_route(a.logits, a.x, a.M, a.k, a.E, a.softcap, a.w_q,
+                                             a.w_scales, a.N, ids, wts, handoff,
+                                             queue + MOE_QUEUE_HANDOFF_STATUS, rows, s)) !=
+            hipSuccess)
+            return e;
+        return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s, handoff,
+                              a.M * a.k);
     }
     if ((e = launch_route(a.logits, a.M, a.E, a.k, a.softcap, ids, wts, s)) != hipSuccess) return e;
     if (!(a.flags & MOE_FWD_STAGED) && forward_fused_applies(a.M, a.k, a.E, a.K, a.N, a.chunk)) {
@@ -647,6 +666,7 @@ int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int f
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
     if (flags & MOE_FWD_STAGED) return 5;
     if (gemm_fp8_tile_applies(K, chunk)) return 5;
+    if (fwd_route_fused(M, E, k, K, N, chunk, flags)) return 2;
     return forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
 

@@ -31,6 +31,21 @@
 //
 // Output.  fp32 rows at their route ids (rows[t*k + j] = x[t] . W[e_tj]^T with both operands
 // dequantised per block), which the combine reads without a slot table.
+//
+// Routing inside (the ROUTE form; [FMF8] "Baseline: 7 kernels" item 1 folded in as well).
+// Token t is routed by wave t / G of workgroup t % G (G workgroups) before that wave waits for
+// anything.  It writes the token's ids and weights for the combine, and each route once more
+// into the handoff words as kRouteTag | expert with an agent-scope store: a word carries its
+// own validity, so no flag, fence or ordering between stores is needed.  Every thread of
+// every workgroup polls its four route words (agent-scope loads, which also fetch the ids it
+// needs) until they carry the tag, at most kMaxPolls rounds.  No wait depends on a workgroup
+// that has not been dispatched: the routing waves wait for nothing first.  A workgroup whose
+// wait gives up sets *status and skips its slices (its rows are not written).  The handoff
+// words must not carry the tag when the kernel starts: the combine that follows clears them.
+// The tag's high half, 0x7FBA, makes a signalling-NaN pattern and a 0x7F byte, which no
+// kernel of this library stores (E4M3 codes never hold 0x7F, computed NaNs are the default
+// one, ids and counts are small), so neither old data nor an earlier step can pass for a
+// fresh route.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -49,6 +64,9 @@ constexpr int kMaxRoutes = 2048;              // M * k
 constexpr int kMaxLocal = 4;                  // experts touched by one workgroup's range
 constexpr int kTiles = 4;                     // resident 16-row tiles
 constexpr int kXSteps = 256 / 4 / kWaves;     // x loads per lane for one tile
+constexpr int kRouteVPL = 4;                  // ROUTE form: logits per lane, E <= 256
+constexpr uint32_t kRouteTag = 0x7FBA0000u;   // high half of a published route word
+constexpr int kMaxPolls = 1 << 18;
 
 struct FusedLds {
     uint4 frag[kTiles][kKB * 2 * 64];         // fragment f = (k-block f/2, half f%2)
@@ -60,6 +78,18 @@ struct FusedLds {
     int trc[kTiles];                          // rows of each resident tile
     int tlb[kTiles];                          // list position of its row 0
     int wsum[2][kWaves];
+    int wave_ok[kWaves];                      // ROUTE form: the wave's routes all arrived
+};
+
+// Arguments of the ROUTE form (unused otherwise).
+struct FusedRoute {
+    const float* logits;                      // f32 [M][E]
+    int32_t* ids;                             // out: topk_ids [M][k]
+    float* weights;                           // out: topk_weights [M][k]
+    uint32_t* handoff;                        // [M*k] route words, no tag at launch
+    uint32_t* status;                         // set to 1 when a wait gives up
+    int M, E;
+    float softcap;
 };
 
 // Workgroup barrier for LDS data only: vector-memory operations stay in flight.
@@ -86,11 +116,11 @@ __device__ __forceinline__ int scan512_small(int c, int* s_w, int& total) {
     return base + below;
 }
 
-template <bool NT>
+template <bool NT, bool ROUTE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, int R, int k,
                            const uint8_t* w, const float* __restrict__ w_scales, int N,
-                           int slices, float* __restrict__ rows_out) {
+                           int slices, float* __restrict__ rows_out, FusedRoute rt) {
     __shared__ FusedLds L;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,6 +130,23 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     const int Nb = N >> 7;                      // 128-row weight-scale blocks per expert
     const int lo = (int)((long long)slices * blockIdx.x / gridDim.x);
     const int hi = (int)((long long)slices * (blockIdx.x + 1) / gridDim.x);
+    if constexpr (ROUTE) {
+        const int t = blockIdx.x + gridDim.x * wave;
+        if (t < rt.M) {                         // wave-uniform: this wave routes token t
+            float val[kRouteVPL];
+            route_load_row<kRouteVPL>(rt.logits + (size_t)t * rt.E, rt.E, lane, val);
+            int my_e;
+            float my_w;
+            route_select<kRouteVPL>(val, rt.E, k, rt.softcap, lane, my_e, my_w);
+            if (lane < k) {
+                const size_t r = (size_t)t * k + lane;
+                __hip_atomic_store(rt.handoff + r, kRouteTag | (uint32_t)my_e,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                rt.ids[r] = my_e;
+                rt.weights[r] = my_w;
+            }
+        }
+    }
     if (lo >= hi) return;                       // whole workgroup
     const int e0 = lo / NS;
     const int ne = (hi - 1) / NS - e0 + 1;      // local experts e0 .. e0+ne-1 (<= kMaxLocal)
@@ -134,15 +181,57 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     constexpr int kPre = 4;
     const int s_pre = min(lo + wave, hi - 1);
     int v[4];
+    if constexpr (!ROUTE) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ids[min(tid * 4 + u, R - 1)];
-    __builtin_amdgcn_sched_barrier(0);          // the ids go out first
-    {
-        const uint8_t* wp = slice_ptr(s_pre);
+        for (int u = 0; u < 4; ++u) v[u] = ids[min(tid * 4 + u, R - 1)];
+        __builtin_amdgcn_sched_barrier(0);      // the ids go out first
+        {
+            const uint8_t* wp = slice_ptr(s_pre);
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) load_unit(wp, u, u);
+            for (int u = 0; u < kPre; ++u) load_unit(wp, u, u);
+        }
+        MOE_WAIT_VMCNT(2 * kPre);               // the ids
+    } else {
+        // the early burst goes out while the routing waves finish; then every thread waits
+        // for its four route words, which bring the ids
+        {
+            const uint8_t* wp = slice_ptr(s_pre);
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) load_unit(wp, u, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        unsigned have = 0;                      // bit u: v[u] arrived
+        int ok = 0;
+        for (int it = 0; it < kMaxPolls; ++it) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!(have >> u & 1u)) {
+                    const uint32_t wd = __hip_atomic_load(rt.handoff + min(tid * 4 + u, R - 1),
+                                                          __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                    if ((wd & 0xFFFF0000u) == kRouteTag) {
+                        v[u] = (int)(wd & 0xFFFFu);
+                        have |= 1u << u;
+                    }
+                }
+            }
+            if (__ballot(have != 15u) == 0) {
+                ok = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) {
+            L.wave_ok[wave] = ok;
+            if (!ok)
+                __hip_atomic_store(rt.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        barrier_lds();
+        int all_ok = 1;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) all_ok &= L.wave_ok[i];
+        if (!__builtin_amdgcn_readfirstlane(all_ok)) return;      // whole workgroup
     }
-    MOE_WAIT_VMCNT(2 * kPre);                   // the ids
 #pragma unroll
     for (int u = 0; u < 4; ++u)                 // local expert index; invalid ids match none
         v[u] = tid * 4 + u < R ? v[u] - e0 : -1;
@@ -375,13 +464,32 @@ bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows) {
            fused_max_local_experts(E, N, device_info().cu_count) <= kMaxLocal;
 }
 
+bool fused_route_applies(int M, int k, int E) {
+    return E <= 64 * kRouteVPL && (long long)M <= (long long)kWaves * device_info().cu_count &&
+           k <= 64;
+}
+
 hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
                                  const uint8_t* w, const float* w_scales, int N,
                                  float* rows_out, hipStream_t s) {
     const int grid = device_info().cu_count;    // one 8-wave workgroup per CU
     const int slices = E * (N / 16);
-    hipLaunchKernelGGL(gemm_fp8_fused_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, ids,
-                       M * k, k, w, w_scales, N, slices, rows_out);
+    const FusedRoute none{};
+    hipLaunchKernelGGL((gemm_fp8_fused_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s,
+                       x, ids, M * k, k, w, w_scales, N, slices, rows_out, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, int M, int k,
+                                       int E, float softcap, const uint8_t* w,
+                                       const float* w_scales, int N, int32_t* ids,
+                                       float* weights, uint32_t* handoff, uint32_t* status,
+                                       float* rows_out, hipStream_t s) {
+    const int grid = device_info().cu_count;    // every token's routing wave is in the grid
+    const int slices = E * (N / 16);
+    const FusedRoute rt{logits, ids, weights, handoff, status, M, E, softcap};
+    hipLaunchKernelGGL((gemm_fp8_fused_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s,
+                       x, nullptr, M * k, k, w, w_scales, N, slices, rows_out, rt);
     return hipGetLastError();
 }
 

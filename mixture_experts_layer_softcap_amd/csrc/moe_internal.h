@@ -123,6 +123,16 @@ bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows);
 hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
                                  const uint8_t* w, const float* w_scales, int N,
                                  float* rows_out, hipStream_t s);
+// The same GEMM with the route inside (moe_route folded in): writes ids and weights, hands
+// the routes over through tagged words handoff [M*k] (untagged at launch; cleared by the
+// combine) and sets *status to 1 if a workgroup's wait gave up.  Applies where
+// fused_route_applies also holds.
+bool fused_route_applies(int M, int k, int E);
+hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, int M, int k,
+                                       int E, float softcap, const uint8_t* w,
+                                       const float* w_scales, int N, int32_t* ids,
+                                       float* weights, uint32_t* handoff, uint32_t* status,
+                                       float* rows_out, hipStream_t s);
 
 // per-expert counts [E] and exclusive offsets [E+1] of the routed ids (E <= 1024)
 hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* counts,
@@ -141,8 +151,9 @@ hipError_t launch_gemm_bf16(const uint16_t* a, int K, const uint16_t* w, int N,
 hipError_t launch_swiglu_quant(const float* h, int R, int I, uint8_t* a_q, float* a_scales,
                                hipStream_t s);
 
+// clear: clear_n words set to zero by the same launch (the route-fused GEMM's flags)
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
-                          hipStream_t s);
+                          hipStream_t s, uint32_t* clear = nullptr, int clear_n = 0);
 
 }  // namespace moe

@@ -26,26 +26,6 @@ namespace {
 constexpr int kRouteWaves = 4;   // tokens (waves) per workgroup at most
 constexpr int kQuantSplit = 2;   // waves quantising one token's row, each a slice of K
 
-// monotone 32-bit image of a logit (the high word of route_key)
-__device__ __forceinline__ uint32_t logit_ord(float v) { return (uint32_t)(route_key(v, 0) >> 32); }
-
-// maximum over the 64 lanes: inclusive max-scans inside each row of 16 lanes (row_shr 1, 2, 4,
-// 8), then the row totals carried across rows (row_bcast 15 into rows 1 and 3, row_bcast 31
-// into rows 2 and 3); lane 63 ends with the wave's maximum.  Lanes a shift leaves without a
-// source take 0, which is below or equal to every image.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define MOE_DPP_MAX(ctrl, rows) \
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rows, 0xf, false))
-    MOE_DPP_MAX(0x111, 0xf);
-    MOE_DPP_MAX(0x112, 0xf);
-    MOE_DPP_MAX(0x114, 0xf);
-    MOE_DPP_MAX(0x118, 0xf);
-    MOE_DPP_MAX(0x142, 0xa);
-    MOE_DPP_MAX(0x143, 0xc);
-#undef MOE_DPP_MAX
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // One wave per token; blockDim.x / 64 tokens per workgroup (one while the batch is smaller than
 // four per CU, so small batches spread over the CUs).
 template <int VPL, bool QUANT>
@@ -100,59 +80,14 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         }
     }
     if (t >= M) return;
-    const float* row = logits + (size_t)t * E;
-
     float val[VPL];
-    uint32_t ord[VPL];
-    uint64_t avail[VPL];                        // experts not yet taken (bit per lane)
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) val[i] = row[min(lane + 64 * i, E - 1)];   // clamped
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        ord[i] = logit_ord(val[i]);
-        avail[i] = __ballot(lane + 64 * i < E);
-    }
-
-    int my_e = 0;
-    float my_l = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        uint32_t loc = 0;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            loc = max(loc, (avail[i] >> lane) & 1ull ? ord[i] : 0u);
-        const uint32_t m = wave_max_u32(loc);
-        // the lowest-index available expert holding the maximum
-        int win_i = -1, win_l = 0;
-#pragma unroll
-        for (int i = VPL - 1; i >= 0; --i) {
-            const uint64_t hit = __ballot(ord[i] == m) & avail[i];
-            if (hit) {
-                win_i = i;
-                win_l = __builtin_ctzll(hit);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (i == win_i) avail[i] &= ~(1ull << win_l);
-        float wl = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (i == win_i) wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), win_l));
-        if (lane == j) {
-            my_e = win_l + 64 * win_i;
-            my_l = wl;
-        }
-    }
-
-    const bool active = lane < k;
-    float c = my_l;
-    if (softcap > 0.0f) c = softcap * tanhf(my_l / softcap);
-    const float c0 = __shfl(c, 0);                         // the largest selected value
-    const float ex = active ? expf(c - c0) : 0.0f;
-    const float sum = wave_sum(ex);
-    if (active) {
+    route_load_row<VPL>(logits + (size_t)t * E, E, lane, val);
+    int my_e;
+    float my_w;
+    route_select<VPL>(val, E, k, softcap, lane, my_e, my_w);
+    if (lane < k) {
         ids[(size_t)t * k + lane] = my_e;
-        weights[(size_t)t * k + lane] = ex / sum;
+        weights[(size_t)t * k + lane] = my_w;
     }
 }
 

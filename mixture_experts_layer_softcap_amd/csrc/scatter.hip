@@ -10,6 +10,8 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -26,10 +28,12 @@ template <bool SLOTS, int CPT, int kGroup>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const float* __restrict__ rows, const int32_t* __restrict__ route_slots,
     const float* __restrict__ weights, const int32_t* __restrict__ ids, int M, int k, int E,
-    int N, uint16_t* __restrict__ out) {
+    int N, uint16_t* __restrict__ out, uint32_t* __restrict__ clear, int clear_n) {
     typedef float vec __attribute__((ext_vector_type(CPT)));
     const int groups = N / CPT;
     const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    // words the step's GEMM has finished with that must start at zero in the next step
+    if (clear && idx < (size_t)clear_n) clear[idx] = 0u;
     if (idx >= (size_t)M * groups) return;
     const int t = (int)(idx / groups);
     const int n = (int)(idx % groups) * CPT;
@@ -72,45 +76,50 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
 template <bool SLOTS, int CPT>
 hipError_t launch_cpt(const float* rows, const int32_t* route_slots, const float* weights,
                       const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
-                      unsigned grid, hipStream_t s) {
+                      unsigned grid, uint32_t* clear, int clear_n, hipStream_t s) {
     if (k <= 2)
         hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 2>), dim3(grid), dim3(kThreads), 0, s,
-                           rows, route_slots, weights, ids, M, k, E, N, out);
+                           rows, route_slots, weights, ids, M, k, E, N, out, clear, clear_n);
     else if (k <= 4)
         hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 4>), dim3(grid), dim3(kThreads), 0, s,
-                           rows, route_slots, weights, ids, M, k, E, N, out);
+                           rows, route_slots, weights, ids, M, k, E, N, out, clear, clear_n);
     else
         hipLaunchKernelGGL((scatter_kernel<SLOTS, CPT, 8>), dim3(grid), dim3(kThreads), 0, s,
-                           rows, route_slots, weights, ids, M, k, E, N, out);
+                           rows, route_slots, weights, ids, M, k, E, N, out, clear, clear_n);
     return hipGetLastError();
 }
 
 template <bool SLOTS>
 hipError_t launch_slots(const float* rows, const int32_t* route_slots, const float* weights,
                         const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
-                        hipStream_t s) {
+                        uint32_t* clear, int clear_n, hipStream_t s) {
     // widest threads that still give one workgroup per CU
     const size_t cus = (size_t)device_info().cu_count;
     int cpt = 4;
     while (cpt > 1 && (N % cpt || (size_t)M * (N / cpt) < cus * kThreads)) cpt >>= 1;
     const size_t work = (size_t)M * (N / cpt);
-    const unsigned grid = (unsigned)((work + kThreads - 1) / kThreads);
+    const unsigned grid = (unsigned)((std::max(work, (size_t)clear_n) + kThreads - 1) / kThreads);
     if (cpt == 4)
-        return launch_cpt<SLOTS, 4>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
+        return launch_cpt<SLOTS, 4>(rows, route_slots, weights, ids, M, k, E, N, out, grid, clear,
+                                      clear_n, s);
     if (cpt == 2)
-        return launch_cpt<SLOTS, 2>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
-    return launch_cpt<SLOTS, 1>(rows, route_slots, weights, ids, M, k, E, N, out, grid, s);
+        return launch_cpt<SLOTS, 2>(rows, route_slots, weights, ids, M, k, E, N, out, grid, clear,
+                                      clear_n, s);
+    return launch_cpt<SLOTS, 1>(rows, route_slots, weights, ids, M, k, E, N, out, grid, clear,
+                                      clear_n, s);
 }
 
 }  // namespace
 
 hipError_t launch_scatter(const float* rows, const int32_t* route_slots, const float* weights,
                           const int32_t* ids, int M, int k, int E, int N, uint16_t* out,
-                          hipStream_t s) {
+                          hipStream_t s, uint32_t* clear, int clear_n) {
     if ((size_t)M * N == 0) return hipSuccess;
     if (route_slots)
-        return launch_slots<true>(rows, route_slots, weights, ids, M, k, E, N, out, s);
-    return launch_slots<false>(rows, route_slots, weights, ids, M, k, E, N, out, s);
+        return launch_slots<true>(rows, route_slots, weights, ids, M, k, E, N, out, clear,
+                                  clear_n, s);
+    return launch_slots<false>(rows, route_slots, weights, ids, M, k, E, N, out, clear, clear_n,
+                               s);
 }
 
 namespace {

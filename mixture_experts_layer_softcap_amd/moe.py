@@ -31,8 +31,10 @@ MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
 MOE_FWD_STAGED = 4
 MOE_FWD_ATOMIC_COMBINE = 64
+MOE_FWD_FUSED_ROUTE = 128
 
 MOE_QUEUE_WORDS = 16
+MOE_QUEUE_HANDOFF_STATUS = 10
 MOE_SCHED_AUTO = -1
 MOE_SCHED_DISPATCH = 0
 MOE_SCHED_STATIC = 1

@@ -889,6 +889,54 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
         assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N} chunk={chunk}")
 
 
+@pytest.mark.parametrize("graph", [False, True])
+@pytest.mark.parametrize("M,E,k,N", [
+    (128, 256, 8, 512),     # the M=128, E=256, top-8 layer
+    (1, 16, 1, 128),        # one token: one routing wave; 128 workgroups without slices exit
+    (8, 16, 2, 256),        # the tiny layer's routing at K = 2048
+    (300, 128, 4, 128),     # more tokens than workgroups: second waves route as well
+    (2048, 128, 1, 128),    # every wave of every workgroup routes a token
+])
+def test_forward_fused_route_matches_three_kernels(M, E, k, N, graph):
+    # the two-kernel step (route inside the small-batch GEMM, ids handed over through flags in
+    # the workspace) against the three-kernel step: the same ids, weights and output bits,
+    # call after call, starting from a workspace full of old bytes; the combine leaves the
+    # flags cleared and the handoff status zero
+    K = 2048
+    d = synth.fused_inputs(M, E, k, K, N, seed=M + 7 * E)
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    flags = moe.MOE_FWD_FUSED_ROUTE | (moe.MOE_FWD_GRAPH if graph else 0)
+    assert moe.forward_kernels(M, E, k, K, N, 0, flags) == 2
+    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True)
+    ws = zeros(moe.forward_workspace_bytes(M, E, k, K, N), torch.uint8)
+    ws.fill_(0xA5)
+    out = zeros((M, N), torch.int16)
+    args = [to_dev(d["logits"]), to_dev(d["x"]), to_dev(d["w_q"]), to_dev(d["w_s"])]
+    R = M * k
+    for rep in range(4):
+        out.fill_(0)
+        moe.forward(*args, k, CAP, out, ws, flags=flags)
+        sync()
+        np.testing.assert_array_equal(to_np(out).view(np.uint16), base[0], f"call {rep}")
+        for part, dt in ((0, np.int32), (1, np.float32)):
+            np.testing.assert_array_equal(ws_part(ws, d, part, dt, R), ws_part(ws3, d, part, dt, R))
+        assert (ws_part(ws, d, 12, np.uint32, R) == 0).all(), "route words left set"
+        assert ws_part(ws, d, 7, np.uint32, moe.MOE_QUEUE_WORDS)[
+            moe.MOE_QUEUE_HANDOFF_STATUS] == 0xA5A5A5A5, "handoff status written"
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
+    assert_bf16_close(base[0], ref["y64"], f"fused route M={M} E={E} k={k} N={N}")
+
+
+def test_forward_fused_route_only_where_it_applies():
+    # E above 256 or a batch outside the small-batch path keeps the route kernel
+    f = moe.MOE_FWD_FUSED_ROUTE
+    assert moe.forward_kernels(100, 300, 3, 2048, 384, 0, f) == 3
+    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, f) == 5
+    assert moe.forward_kernels(1024, 256, 8, 2048, 512, 0, f) == 5
+    assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, f | moe.MOE_FWD_STAGED) == 5
+
+
 def test_forward_repeat_determinism():
     d = workload(QWEN)
     outs = gpu_forward(d, reps=20)

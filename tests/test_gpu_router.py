@@ -65,6 +65,11 @@ def check_logits(y, ref64, x, wg, what):
     (37, 192, 10),        # ragged tokens and experts, 3 k steps
     (1, 64, 1),           # one token, one expert, one k step
     (300, 320, 1000),     # many experts, E not a multiple of 16 or 64
+    # tile shapes the launcher picks on a 256-CU chip (16*TB tokens x 16*EB experts):
+    (2048, 256, 256),     # 32 x 64 tiles, expert blocks spread over the 8 XCDs
+    (4100, 128, 200),     # 64 x 64 tiles, ragged tokens and experts, 4 expert blocks
+    (4096, 128, 512),     # 64 x 64 tiles, 8 expert blocks (one per XCD)
+    (16384, 128, 8),      # 64 x 16 tiles, 8 experts padded to 16 gate rows
 ])
 def test_router_logits_match_oracle(M, H, E):
     d = synth.router_inputs(M, H, E, seed=M + E)
