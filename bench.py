@@ -376,7 +376,7 @@ def bench_mlp(args, moe, synth, torch, np):
 
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if H <= 8192 else 64))
-    fused = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows) == 6
+    fused = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows) == 5
     h1 = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
     if fused:
         # the gate+up GEMM alone, straight from the routed ids the last step left (part 0)
@@ -438,9 +438,9 @@ def bench_mlp(args, moe, synth, torch, np):
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "H": H, "I": I,
                    "softcap": cap, "weight_copies_rotated": copies, "chunk_rows": chunk,
-                   "path": ("6 kernels: route, layout (down tasks, sorted ids), gate+up GEMM "
-                            "from the routed ids, silu*up requantise, down GEMM gathering by "
-                            "sorted id, combine" if fused else
+                   "path": ("5 kernels: route, gate+up GEMM from the routed ids, layout (down "
+                            "tasks, sorted ids) with silu*up requantise in one launch, down GEMM "
+                            "gathering by sorted id, combine" if fused else
                             "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "
                             "silu*up requantise, down GEMM, combine")},
         "effective_tflops": round(flops / (us * 1e-6) / 1e12, 3),

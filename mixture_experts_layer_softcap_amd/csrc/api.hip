@@ -792,7 +792,7 @@ int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows) {
     int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, H);
     if (!chunk_rows && chunk > 64 && Kmax > 8192) chunk = 64;
     return forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)
-               ? 6
+               ? 5
                : 7;
 }
 
@@ -841,14 +841,15 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     hipError_t e;
     if (forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)) {
         // small batch: the gate+up GEMM straight from the routed ids (layout, gather and
-        // quantisation of x inside) with rows at route ids; the activations stay in route
-        // order and the down GEMM gathers its rows by sorted route id
+        // quantisation of x inside) with rows at route ids; the down projection's layout
+        // shares a launch with the activation step; the activations stay in route order and
+        // the down GEMM gathers its rows by sorted route id
         if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
-            (e = launch_layout(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td, mtd,
-                               nt + 1, queue2, sorted, nullptr, s)) != hipSuccess ||
             (e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s)) !=
                 hipSuccess ||
-            (e = launch_swiglu_quant(h1, R, I, aq, as, s)) != hipSuccess ||
+            (e = launch_layout_swiglu(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td,
+                                      nt + 1, queue2, sorted, h1, I, aq, as, s)) !=
+                hipSuccess ||
             (e = launch_gemm_fp8_range(aq, as, R, I, w2_q, w2_scales, H, td, nt + 1, mtd,
                                        MOE_EPI_ROUTE_F32, sorted, h2, s, sorted)) !=
                 hipSuccess ||

@@ -56,6 +56,13 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
                          int32_t* sorted_route_ids, int32_t* route_slots, hipStream_t s);
 
 // one layout pass writing two task lists over the same chunks (n_blocks and n_blocks2 panels)
+// The FP8 MLP's layout (sorted route ids, one task list) and its activation step
+// (moe_swiglu_quant on h [M*k][2I]) in one launch.
+hipError_t launch_layout_swiglu(const int32_t* ids, int M, int k, int E, int n_blocks,
+                                int chunk_rows, int32_t* counts, int32_t* offsets,
+                                int32_t* cursors, moe_task* tasks, int32_t* ntasks,
+                                uint32_t* queue, int32_t* sorted_route_ids, const float* h,
+                                int I, uint8_t* a_q, float* a_scales, hipStream_t s);
 hipError_t launch_layout2(const int32_t* ids, int M, int k, int E, int chunk_rows,
                           int32_t* counts, int32_t* offsets, int32_t* cursors, int n_blocks,
                           moe_task* tasks, int32_t* ntasks, uint32_t* queue, int n_blocks2,
