@@ -307,15 +307,18 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
                 L.tlb[t] = lb;
             }
             // step st covers blocks 4*st .. 4*st+3 (row b>>4, k-block b&15), one per 16 lanes;
-            // rows past rc load row 0 again and are not quantised (their columns are not stored)
+            // rows past rc are not quantised (their columns are not stored); their lanes still
+            // load, unconditionally, but all from the first 256 bytes of x, which stay in the
+            // CU's L1 and take no place among its requests to L2 (at a few routes per expert
+            // most of a tile is padding)
             uint4 xr[kXSteps];
 #pragma unroll
             for (int i8 = 0; i8 < kXSteps; ++i8) {
                 const int bq = (wave + i8 * kWaves) * 4 + g;
                 const int jj = bq >> 4, kb = bq & 15;
                 const int ent = L.list[lb + (jj < rc ? jj : 0)];
-                xr[i8] = *reinterpret_cast<const uint4*>(x + (size_t)(ent >> 12) * kK + kb * 128 +
-                                                         j * 8);
+                const size_t off = jj < rc ? (size_t)(ent >> 12) * kK + kb * 128 : 0;
+                xr[i8] = *reinterpret_cast<const uint4*>(x + off + j * 8);
             }
             MOE_WAIT_VMCNT(0);
             if (BURST) {
