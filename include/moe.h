@@ -103,8 +103,9 @@ int moe_device_check(void);
 /* ---- [WEAVE] section 3.1 (the gate, counted in the layer's forward): router projection ---
  * x bf16 [M][H] (the layer's hidden states), w_gate bf16 [E][H] -> logits f32 [M][E]:
  *   logits[t][e] = sum_h x[t][h] * w_gate[e][h]   (bf16 products, fp32 accumulation)
- * the input of moe_route / moe_forward.  H a multiple of 64, 1 <= E <= 1024.  The fp32 sum is
- * taken in a fixed order (repeat calls give the same bits).  One launch on `stream`. */
+ * the input of moe_route / moe_forward.  H a multiple of 64, 1 <= E <= 1024, M*H < 2^40 and
+ * ceil(M/16)*ceil(E/16) < 2^31 (else MOE_E_INVAL).  The fp32 sum is taken in a fixed order
+ * (repeat calls give the same bits).  One launch on `stream`. */
 int moe_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
                       float* logits, moe_stream_t stream);
 

@@ -438,6 +438,7 @@ int moe_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, i
                       float* logits, moe_stream_t stream) {
     if (M < 0 || H < 64 || H % 64 || E < 1 || E > kMaxE || (long long)M * H >= (1LL << 40))
         return MOE_E_INVAL;
+    if ((long long)((M + 15) / 16) * ((E + 15) / 16) > 0x7FFFFFFFLL) return MOE_E_INVAL;
     if (M > 0 && (!x || !w_gate || !logits)) return MOE_E_INVAL;
     int rc = check_device();
     if (rc) return rc;

@@ -156,6 +156,7 @@ void router_launch(const uint16_t* x, int M, int H, const uint16_t* w_gate, int 
 hipError_t launch_router_logits(const uint16_t* x, int M, int H, const uint16_t* w_gate, int E,
                                 float* logits, hipStream_t s) {
     if (M == 0) return hipSuccess;
+    if (router_grid<1, 1>(M, E) > 0x7FFFFFFFLL) return hipErrorInvalidValue;   // one grid
     // the largest tile (fewest bytes per logit) whose grid still covers every CU
     const long long cus = device_info().cu_count;
     if (E > 32 && router_grid<4, 4>(M, E) >= cus) {

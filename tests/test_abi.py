@@ -194,3 +194,4 @@ def test_router_logits_rejects_on_the_host(L):
     assert rl(NULL, 8, 128, P, 4, P, S) == INVAL       # null x
     assert rl(P, 8, 128, P, 4, NULL, S) == INVAL       # null logits
     assert rl(P, -1, 128, P, 4, P, S) == INVAL
+    assert rl(P, 2 ** 30, 64, P, 1024, P, S) == INVAL  # 2^26 x 64 workgroups
