@@ -928,6 +928,33 @@ def test_forward_fused_route_matches_three_kernels(M, E, k, N, graph):
     assert_bf16_close(base[0], ref["y64"], f"fused route M={M} E={E} k={k} N={N}")
 
 
+def test_forward_fused_route_ties_and_non_finite_logits():
+    # the route inside the GEMM follows the route's order on crafted rows: all tied, ten tied
+    # above the rest (the k/k+1 boundary), NaN (below every number) and +inf logits; ids
+    # against the oracle's route, output bits against the three-kernel step
+    M, E, k, K, N = 16, 64, 4, 2048, 128
+    d = synth.fused_inputs(M, E, k, K, N, seed=5)
+    lg = d["logits"]
+    lg[0, :] = 1.0
+    lg[1, 10:20] = 3.0
+    lg[2, :] = np.nan
+    lg[2, 7] = -5.0
+    lg[3, ::2] = np.nan
+    lg[4, 60:] = np.inf
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    f = moe.MOE_FWD_FUSED_ROUTE
+    assert moe.forward_kernels(M, E, k, K, N, 0, f) == 2
+    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True)
+    (got, ws2) = gpu_forward(d, flags=f, reps=2, keep_ws=True)
+    R = M * k
+    r_ids, _ = orc.route(lg, k, CAP)
+    np.testing.assert_array_equal(ws_part(ws2, d, 0, np.int32, R).reshape(M, k), r_ids)
+    np.testing.assert_array_equal(ws_part(ws3, d, 0, np.int32, R).reshape(M, k), r_ids)
+    for y in got:
+        np.testing.assert_array_equal(y, base[0])
+
+
 def test_forward_fused_route_only_where_it_applies():
     # E above 256 or a batch outside the small-batch path keeps the route kernel
     f = moe.MOE_FWD_FUSED_ROUTE
