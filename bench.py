@@ -211,6 +211,48 @@ def bench_bf16_gemm(args, moe, synth, torch, np):
     print(json.dumps(result))
 
 
+def bench_dense_library(args, synth, torch, np):
+    """--workload bf16_dense_library_<up|down>_rows<R>: context for the grouped GEMM, never a
+    path of this library.  The same compact rows as ONE dense bf16 GEMM [rows,K] x [K,N]
+    (expert 0's weights as the right operand, contiguous) through torch.mm, i.e. the vendor
+    GEMM library, with fp32 accumulation: the best case a library reaches on this shape with
+    no grouping, no partial chunks and no gather."""
+    _, _, _, proj, rows_s = args.workload.split("_")
+    N, K = BF16_GEMMS[proj]
+    rows = int(rows_s[4:])
+    d = synth.grouped_gemm_inputs(rows, 1, N, K, "balanced", seed=0)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(d["A"].view(np.int16)).to(dev).view(torch.bfloat16)
+    b = torch.from_numpy(d["W"][0].view(np.int16)).to(dev).view(torch.bfloat16).t().contiguous()
+    out = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        torch.mm(a, b, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        torch.mm(a, b, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    tflops = 2.0 * rows * N * K / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "µs per dense BF16 GEMM through torch.mm (library reference, context only)",
+        "value": round(us, 3), "unit": "us/gemm", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "N": N, "K": K,
+                   "library": f"torch {torch.__version__} mm"},
+        "effective_tflops": round(tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "library GEMM", "achieved": round(tflops, 2),
+                     "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(us, 3)},
+    }))
+
+
 def bench_ffn(args, moe, synth, torch, np):
     """--workload ffn_mixtral_T<T>[_uniform]: the whole Mixtral-like expert FFN layer (E=8,
     top-2, hidden 4096, FFN 1024, bf16), router logits skewed by -1.1 ln(e+1) unless
@@ -522,6 +564,9 @@ def main():
 
     if args.workload.startswith("bf16_grouped_gemm_"):
         bench_bf16_gemm(args, moe, synth, torch, np)
+        return
+    if args.workload.startswith("bf16_dense_library_"):
+        bench_dense_library(args, synth, torch, np)
         return
     if args.workload.startswith("ffn_mixtral_"):
         bench_ffn(args, moe, synth, torch, np)
