@@ -719,8 +719,8 @@ def main():
                             if nkern == 2
                             else "3 kernels: route, grouped GEMM from the routed ids, combine"
                             if fused
-                            else "5 kernels: route+quantise, count, sort+layout, gathering "
-                                 "grouped GEMM, combine" if gather
+                            else "4 kernels: route+quantise, layout, gathering grouped GEMM, "
+                                 "combine" if gather
                             else "5 kernels: route, layout, QSG, grouped GEMM, combine"),
                    "gemm_task_walk": ("weight slices split evenly over the CUs" if fused
                                       else "contiguous ranges, per-wave pull"

@@ -276,7 +276,7 @@ size_t moe_forward_workspace_bytes(int M, int E, int k, int K, int N);
 /* Byte offset inside the workspace of one intermediate, for inspection in tests:
  * 0 topk_ids, 1 topk_weights, 2 counts, 3 offsets, 4 cursors, 5 tasks, 6 ntasks, 7 queue,
  * 8 sorted_route_ids, 9 a_q, 10 a_scales, 11 GEMM rows (at route ids), 12 route_slots,
- * 13 x_q (token-major codes), 14 x_scales, 15 slot cursors.  -1 on bad arguments. */
+ * 13 x_q (token-major codes), 14 x_scales.  -1 on bad arguments. */
 int64_t moe_forward_workspace_offset(int M, int E, int k, int K, int N, int which);
 
 /* logits f32 [M][E], x bf16 [M][K], w_q E4M3 [E][N][K], w_scales f32 [E][N/128][K/128]
@@ -331,7 +331,7 @@ int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    int flags, moe_stream_t stream);
 
 /* Number of kernels moe_forward_ex launches for these arguments: 2 (small batch with
- * MOE_FWD_FUSED_ROUTE), 3 (small batch) or 5 (the gathering path or the staged one);
+ * MOE_FWD_FUSED_ROUTE), 3 (small batch), 4 (the gathering path) or 5 (the staged one);
  * MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 
@@ -361,8 +361,8 @@ int moe_forward_noalloc(const float* logits, const uint16_t* x, const uint8_t* w
  * w_down bf16 [E][H][F] -> out bf16 [M][H].  H a multiple of 256, F of 128.  Workspace of
  * moe_ffn_workspace_bytes(...) bytes; parts (for inspection): 0 topk_ids, 1 topk_weights,
  * 2 counts, 3 offsets, 4 cursors, 5 up tasks, 6 down tasks, 7 ntasks, 8 sorted_route_ids,
- * 9 route_slots, 10 per-expert slot cursors of the layout, 11 act, 12 down rows, 13 task
- * counters (MOE_QUEUE_WORDS per GEMM).  Six plain launches on `stream`, no host
+ * 9 route_slots, 10 act, 11 down rows, 12 task counters (MOE_QUEUE_WORDS per GEMM).  Five
+ * plain launches on `stream`, no host
  * synchronisation.  flags: only MOE_FWD_SCHED(...) bits, the schedule of both BF16 GEMMs
  * (0: the default). */
 size_t moe_ffn_workspace_bytes(int M, int E, int k, int H, int F);

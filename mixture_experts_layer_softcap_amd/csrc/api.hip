@@ -67,7 +67,7 @@ long long max_tasks_ll(int M, int k, int E, int n_blocks, int chunk_rows) {
 }
 
 // ---- workspace of moe_forward ----------------------------------------------------------
-constexpr int kWsParts = 16;
+constexpr int kWsParts = 15;
 struct WsLayout {
     size_t off[kWsParts];
     size_t total;
@@ -95,7 +95,6 @@ WsLayout ws_layout(int M, int E, int k, int K, int N) {
         R * 4,                      // 12 route_slots
         (size_t)M * K,              // 13 x_q (token-major codes)
         (size_t)(K / 128) * M * 4,  // 14 x_scales
-        (size_t)E * 4,              // 15 per-expert slot cursors of the wide layout
     };
     WsLayout L;
     size_t p = 0;
@@ -180,16 +179,15 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         // routes; the tiled GEMM gathers each routed row from the token-major codes
         uint8_t* x_q = reinterpret_cast<uint8_t*>(at(13));
         float* x_s = reinterpret_cast<float*>(at(14));
-        int32_t* rel = reinterpret_cast<int32_t*>(at(15));
         // the scatter-add form accumulates into fp32 token rows [M][N] (in the rows' space),
         // zeroed by the route kernel
         const bool atomic = a.flags & MOE_FWD_ATOMIC_COMBINE;
-        if ((e = launch_route_quantize_zero(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids,
-                                            wts, x_q, x_s, counts, rel, a.E, s,
-                                            atomic ? rows : nullptr, a.N)) != hipSuccess)
+        if ((e = launch_route_quantize(a.logits, a.x, a.M, a.E, a.k, a.K, a.softcap, ids, wts,
+                                       x_q, x_s, s, atomic ? rows : nullptr, a.N)) !=
+            hipSuccess)
             return e;
         if ((e = launch_layout_sorted_wide(ids, a.M, a.k, a.E, Nb, a.chunk, counts, offsets,
-                                           cursors, tasks, ntasks, queue, rel, sorted, s)) !=
+                                           cursors, tasks, ntasks, queue, sorted, s)) !=
             hipSuccess)
             return e;
         if (atomic) {
@@ -324,7 +322,7 @@ int noalloc_scratch(void** out) {
 const DeviceInfo& device_info() { return g_dev[t_dev].info; }
 
 // ---- Mixtral-like expert FFN layer (BF16) ---------------------------------------------
-constexpr int kFfnParts = 14;
+constexpr int kFfnParts = 13;
 struct FfnLayout {
     size_t off[kFfnParts];
     size_t total;
@@ -348,10 +346,9 @@ FfnLayout ffn_layout(int M, int E, int k, int H, int F) {
         16,                        // 7 ntasks (up, down)
         R * 4,                     // 8 sorted_route_ids
         R * 4,                     // 9 route_slots
-        (size_t)E * 4,             // 10 per-expert slot cursors of the wide layout
-        R * (size_t)F * 2,         // 11 act = silu(gate) * up, bf16 [R][F]
-        R * (size_t)H * 4,         // 12 down-projection rows, f32 [R][H]
-        2 * MOE_QUEUE_WORDS * 4,   // 13 task counters of the two GEMMs
+        R * (size_t)F * 2,         // 10 act = silu(gate) * up, bf16 [R][F]
+        R * (size_t)H * 4,         // 11 down-projection rows, f32 [R][H]
+        2 * MOE_QUEUE_WORDS * 4,   // 12 task counters of the two GEMMs
     };
     FfnLayout L;
     size_t p = 0;
@@ -666,7 +663,7 @@ int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int f
     if (rc) return rc;
     const int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, K);
     if (flags & MOE_FWD_STAGED) return 5;
-    if (gemm_fp8_tile_applies(K, chunk)) return 5;
+    if (gemm_fp8_tile_applies(K, chunk)) return 4;
     if (fwd_route_fused(M, E, k, K, N, chunk, flags)) return 2;
     return forward_fused_applies(M, k, E, K, N, chunk) ? 3 : 5;
 }
@@ -736,22 +733,21 @@ int moe_ffn_forward(const float* logits, const uint16_t* x, const uint16_t* w_up
     int32_t* nt = reinterpret_cast<int32_t*>(at(7));
     int32_t* sorted = reinterpret_cast<int32_t*>(at(8));
     int32_t* slots = reinterpret_cast<int32_t*>(at(9));
-    int32_t* rel = reinterpret_cast<int32_t*>(at(10));
-    uint16_t* act = reinterpret_cast<uint16_t*>(at(11));
-    float* down = reinterpret_cast<float*>(at(12));
-    uint32_t* queue = reinterpret_cast<uint32_t*>(at(13));
+    uint16_t* act = reinterpret_cast<uint16_t*>(at(10));
+    float* down = reinterpret_cast<float*>(at(11));
+    uint32_t* queue = reinterpret_cast<uint32_t*>(at(12));
     const int nbu = 2 * F / 256, nbd = H / 256;
     const int mtu = (int)max_tasks_ll(M, k, E, nbu, chunk);
     const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    // route (clearing the layout's counters); count + sort over many workgroups (sorted route
-    // ids, route -> slot, both task lists); gated-up GEMM gathering its rows from x on load
-    // with the SwiGLU epilogue; down GEMM; combine through the slot table
-    if ((e = launch_route_zero(logits, M, E, k, softcap, ids, wts, counts, rel, E, s)) !=
+    // route; the layout over many workgroups in one launch (sorted route ids, route -> slot,
+    // both task lists); gated-up GEMM gathering its rows from x on load with the SwiGLU
+    // epilogue; down GEMM; combine through the slot table
+    if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) !=
             hipSuccess ||
         (e = launch_layout_sorted_wide(ids, M, k, E, nbu, chunk, counts, offsets, cursors, tu,
-                                       nt, queue, rel, sorted, s, slots, nbd, td, nt + 1,
+                                       nt, queue, sorted, s, slots, nbd, td, nt + 1,
                                        queue + MOE_QUEUE_WORDS)) != hipSuccess ||
         (e = launch_gemm_bf16(x, H, w_up, 2 * F, tu, nt, mtu, MOE_EPI_SWIGLU_BF16, act, s,
                               sorted, k, sched, queue)) != hipSuccess ||

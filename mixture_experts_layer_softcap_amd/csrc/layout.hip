@@ -266,48 +266,83 @@ __global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restr
 
 // ---- the same layout over many workgroups (the forward's larger batches) ------------------
 // A single workgroup is bound by its own CU's requests in flight; here every workgroup takes
-// kThreads routes, one per thread.  count_kernel adds each chunk's LDS histogram into counts
-// (zeroed by the preceding route kernel); sort_layout_kernel recomputes the offsets in every
-// workgroup from the counts, workgroup 0 writes offsets, cursors, the task list, ntasks and
-// the queue reset as layout_kernel does, and each chunk reserves its slots inside every expert
-// segment with one returning atomic per expert on rel (zeroed likewise), then places its own
-// routes by their LDS ranks.  The chunks' order inside a segment follows their atomics.
-
-__global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restrict__ ids, int R,
-                                                         int E, int32_t* __restrict__ counts) {
-    __shared__ int s_h[kThreads];
-    const int tid = threadIdx.x;
-    const int r = blockIdx.x * kThreads + tid;
-    const int e = r < R ? ids[r] : -1;
-    s_h[tid] = 0;
-    __syncthreads();
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_h[e], 1);
-    __syncthreads();
-    if (tid < E && s_h[tid] > 0) atomicAdd(&counts[tid], s_h[tid]);
-}
-
-__global__ __launch_bounds__(kThreads) void sort_layout_kernel(
+// the kThreads routes of its chunk, one per thread, in one launch with no exchange between
+// workgroups.  Each workgroup histograms ALL routes' ids in LDS, and separately those of the
+// chunks before its own: the expert totals (hence offsets, the task list, and for workgroup 0
+// counts, cursors, ntasks and the queue reset as layout_kernel writes them) and the chunk's
+// first slot inside every expert segment follow locally, with no global atomics and nothing to
+// clear beforehand.  Inside the chunk a route's rank among the routes of its expert is stable:
+// wave ballots find the lanes holding the same id, and the per-wave counts are prefixed in
+// wave order.  Every segment therefore holds its routes in ascending route id, the order of
+// the serial counting sort ([FMF8] Baseline item 5).
+__global__ __launch_bounds__(kThreads) void layout_wide_kernel(
     const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ cursors, moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks,
-    uint32_t* __restrict__ queue, int32_t* __restrict__ rel,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
+    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue,
     int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots, int n_blocks2,
     moe_task* __restrict__ tasks2, int32_t* __restrict__ ntasks2, uint32_t* __restrict__ queue2) {
-    __shared__ int s_h[kThreads];
-    __shared__ int s_base[kThreads];
+    __shared__ int s_all[kThreads];               // routes per expert, whole batch
+    __shared__ int s_before[kThreads];            // routes per expert in the chunks before this one
+    __shared__ int s_first[kThreads];             // this chunk's first slot in each segment
     __shared__ int s_hist[kThreads];
     __shared__ int s_wsum[kWaves + 1];
+    __shared__ int s_wcnt[kWaves * kThreads];     // [wave][expert]: count, then wave prefix
     const int tid = threadIdx.x;
-    const int r = blockIdx.x * kThreads + tid;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cb = blockIdx.x * kThreads;         // the chunk's first route
+    const int r = cb + tid;
     const int e = r < R ? ids[r] : -1;
-    const int c = tid < E ? counts[tid] : 0;
-    s_h[tid] = 0;
+    s_all[tid] = 0;
+    s_before[tid] = 0;
     s_hist[tid] = 0;
+    for (int i = tid; i < kWaves * E; i += kThreads) s_wcnt[i] = 0;
     __syncthreads();
-    const int rank = (unsigned)e < (unsigned)E ? atomicAdd(&s_h[e], 1) : -1;
+
+    // stable rank inside the wave: lanes whose value v (E for a route past R or an invalid id)
+    // agrees with this lane's in every bit
+    const int v = (unsigned)e < (unsigned)E ? e : E;
+    const int nbits = 32 - __clz(E);
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (v >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+    }
+    const int rank_w = __popcll(same & ((1ull << lane) - 1ull));
+    if (v < E && rank_w == 0) s_wcnt[wave * E + v] = __popcll(same);
+
+    // histograms of the whole batch and of the routes before this chunk (four loads in flight
+    // per thread ahead of their LDS atomics)
+    for (int r0 = 0; r0 < R; r0 += 4 * kThreads) {
+        int q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rr = r0 + u * kThreads + tid;
+            q[u] = rr < R ? ids[rr] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if ((unsigned)q[u] < (unsigned)E) {
+                atomicAdd(&s_all[q[u]], 1);
+                if (r0 + u * kThreads + tid < cb) atomicAdd(&s_before[q[u]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < E) {                                // prefix of the wave counts, in wave order
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int t = s_wcnt[w * E + tid];
+            s_wcnt[w * E + tid] = run;
+            run += t;
+        }
+    }
+    const int c = tid < E ? s_all[tid] : 0;
     int total_rows;
     const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
+    if (tid < E) s_first[tid] = row0 + s_before[tid];
     if (blockIdx.x == 0) {
+        if (tid < E) counts[tid] = c;
         write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
                     s_wsum);
         if (tasks2) {                             // a second list over the same chunks
@@ -318,10 +353,12 @@ __global__ __launch_bounds__(kThreads) void sort_layout_kernel(
                         s_hist, s_wsum);
         }
     }
-    if (tid < E && s_h[tid] > 0) s_base[tid] = row0 + atomicAdd(&rel[tid], s_h[tid]);
     __syncthreads();
-    if (rank >= 0) sorted_route_ids[s_base[e] + rank] = r;
-    if (route_slots && r < R) route_slots[r] = rank >= 0 ? s_base[e] + rank : -1;
+    if (r < R) {
+        const int slot = v < E ? s_first[v] + s_wcnt[wave * E + v] + rank_w : -1;
+        if (slot >= 0) sorted_route_ids[slot] = r;
+        if (route_slots) route_slots[r] = slot;
+    }
 }
 
 }  // namespace
@@ -364,17 +401,14 @@ hipError_t launch_layout2(const int32_t* ids, int M, int k, int E, int chunk_row
 hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, int n_blocks,
                                      int chunk_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* cursors, moe_task* tasks, int32_t* ntasks,
-                                     uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
-                                     hipStream_t s, int32_t* route_slots, int n_blocks2,
-                                     moe_task* tasks2, int32_t* ntasks2, uint32_t* queue2) {
+                                     uint32_t* queue, int32_t* sorted_route_ids, hipStream_t s,
+                                     int32_t* route_slots, int n_blocks2, moe_task* tasks2,
+                                     int32_t* ntasks2, uint32_t* queue2) {
     const int R = M * k;
     if (R == 0) return hipSuccess;
     const unsigned grid = (unsigned)((R + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(count_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E, counts);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sort_layout_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
-                       n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue, rel,
+    hipLaunchKernelGGL(layout_wide_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
+                       n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
                        sorted_route_ids, route_slots, n_blocks2, tasks2, ntasks2, queue2);
     return hipGetLastError();
 }

@@ -21,30 +21,21 @@ hipError_t launch_router_logits(const uint16_t* x, int M, int H, const uint16_t*
 
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap,
                         int32_t* ids, float* weights, hipStream_t s);
-// the same, with zero0[0..zero_n) and zero1[0..zero_n) cleared by its first workgroup
-hipError_t launch_route_zero(const float* logits, int M, int E, int k, float softcap,
-                             int32_t* ids, float* weights, int32_t* zero0, int32_t* zero1,
-                             int zero_n, hipStream_t s);
 
-// route + per-token quantisation of x (token-major codes [M][K], scales [K/128][M])
+// route + per-token quantisation of x (token-major codes [M][K], scales [K/128][M]); with
+// acc != nullptr also zeroes the fp32 accumulator rows acc [M][acc_n] (acc_n % 4 == 0)
 hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
                                  int K, float softcap, int32_t* ids, float* weights,
-                                 uint8_t* x_q, float* x_scales, hipStream_t s);
+                                 uint8_t* x_q, float* x_scales, hipStream_t s,
+                                 float* acc = nullptr, int acc_n = 0);
 
-// the same, also zeroing zero0[0..zero_n) and zero1[0..zero_n) (scratch of the wide layout)
-// and, with acc != nullptr, the fp32 accumulator rows acc [M][acc_n] (acc_n % 4 == 0)
-hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
-                                      int k, int K, float softcap, int32_t* ids, float* weights,
-                                      uint8_t* x_q, float* x_scales, int32_t* zero0,
-                                      int32_t* zero1, int zero_n, hipStream_t s,
-                                      float* acc = nullptr, int acc_n = 0);
-
-// the layout with the sorted route ids over many workgroups: counts and rel [E] must be zero;
-// optionally route -> slot and a second task list over the same chunks (n_blocks2 panels)
+// the layout with the sorted route ids (ascending route id inside each segment) over many
+// workgroups, one launch, E <= 1024; optionally route -> slot and a second task list over the
+// same chunks (n_blocks2 panels)
 hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, int n_blocks,
                                      int chunk_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* cursors, moe_task* tasks, int32_t* ntasks,
-                                     uint32_t* queue, int32_t* rel, int32_t* sorted_route_ids,
+                                     uint32_t* queue, int32_t* sorted_route_ids,
                                      hipStream_t s, int32_t* route_slots = nullptr,
                                      int n_blocks2 = 0, moe_task* tasks2 = nullptr,
                                      int32_t* ntasks2 = nullptr, uint32_t* queue2 = nullptr);

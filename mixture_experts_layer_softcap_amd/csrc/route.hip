@@ -32,8 +32,8 @@ template <int VPL, bool QUANT>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, float softcap,
     int32_t* __restrict__ ids, float* __restrict__ weights, const uint16_t* __restrict__ x,
-    int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales, int32_t* __restrict__ zero0,
-    int32_t* __restrict__ zero1, int zero_n, float* __restrict__ acc, int acc_n) {
+    int K, uint8_t* __restrict__ x_q, float* __restrict__ x_scales, float* __restrict__ acc,
+    int acc_n) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (QUANT && blockIdx.y > 0) {
@@ -72,13 +72,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         }
         return;
     }
-    // scratch the next kernels accumulate into (per-expert counts and cursors)
-    if (zero0 && blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < zero_n; i += blockDim.x) {
-            zero0[i] = 0;
-            zero1[i] = 0;
-        }
-    }
     if (t >= M) return;
     float val[VPL];
     route_load_row<VPL>(logits + (size_t)t * E, E, lane, val);
@@ -94,27 +87,25 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                       float* weights, const uint16_t* x, int K, uint8_t* x_q, float* x_scales,
-                      int32_t* z0, int32_t* z1, int zn, float* acc, int acc_n, hipStream_t s) {
+                      float* acc, int acc_n, hipStream_t s) {
     const int per = M >= kRouteWaves * device_info().cu_count ? kRouteWaves : 1;
     const int grid = (M + per - 1) / per;
     if (x_q)
         hipLaunchKernelGGL((route_kernel<VPL, true>), dim3(grid, 1 + kQuantSplit),
                            dim3(64 * per), 0, s, logits, M, E, k, softcap, ids, weights, x, K, x_q,
-                           x_scales, z0, z1, zn, acc, acc_n);
+                           x_scales, acc, acc_n);
     else
         hipLaunchKernelGGL((route_kernel<VPL, false>), dim3(grid), dim3(64 * per), 0, s,
-                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0,
-                           z1, zn, acc, acc_n);
+                           logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, acc,
+                           acc_n);
     return hipGetLastError();
 }
 
 hipError_t launch_route_any(const float* logits, int M, int E, int k, float softcap,
                             int32_t* ids, float* weights, const uint16_t* x, int K,
-                            uint8_t* x_q, float* x_scales, int32_t* z0, int32_t* z1, int zn,
-                            hipStream_t s, float* acc = nullptr, int acc_n = 0) {
+                            uint8_t* x_q, float* x_scales, float* acc, int acc_n, hipStream_t s) {
     if (M == 0) return hipSuccess;
-#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, z0, z1, zn, \
-                       acc, acc_n, s
+#define MOE_ROUTE_ARGS logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, acc, acc_n, s
     if (E <= 64) return launch_vpl<1>(MOE_ROUTE_ARGS);
     if (E <= 128) return launch_vpl<2>(MOE_ROUTE_ARGS);
     if (E <= 256) return launch_vpl<4>(MOE_ROUTE_ARGS);
@@ -128,30 +119,15 @@ hipError_t launch_route_any(const float* logits, int M, int E, int k, float soft
 hipError_t launch_route(const float* logits, int M, int E, int k, float softcap, int32_t* ids,
                         float* weights, hipStream_t s) {
     return launch_route_any(logits, M, E, k, softcap, ids, weights, nullptr, 0, nullptr,
-                            nullptr, nullptr, nullptr, 0, s);
-}
-
-hipError_t launch_route_zero(const float* logits, int M, int E, int k, float softcap,
-                             int32_t* ids, float* weights, int32_t* zero0, int32_t* zero1,
-                             int zero_n, hipStream_t s) {
-    return launch_route_any(logits, M, E, k, softcap, ids, weights, nullptr, 0, nullptr,
-                            nullptr, zero0, zero1, zero_n, s);
+                            nullptr, nullptr, 0, s);
 }
 
 hipError_t launch_route_quantize(const float* logits, const uint16_t* x, int M, int E, int k,
                                  int K, float softcap, int32_t* ids, float* weights,
-                                 uint8_t* x_q, float* x_scales, hipStream_t s) {
-    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales,
-                            nullptr, nullptr, 0, s);
-}
-
-hipError_t launch_route_quantize_zero(const float* logits, const uint16_t* x, int M, int E,
-                                      int k, int K, float softcap, int32_t* ids, float* weights,
-                                      uint8_t* x_q, float* x_scales, int32_t* zero0,
-                                      int32_t* zero1, int zero_n, hipStream_t s, float* acc,
-                                      int acc_n) {
-    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, zero0,
-                            zero1, zero_n, s, acc, acc_n);
+                                 uint8_t* x_q, float* x_scales, hipStream_t s, float* acc,
+                                 int acc_n) {
+    return launch_route_any(logits, M, E, k, softcap, ids, weights, x, K, x_q, x_scales, acc,
+                            acc_n, s);
 }
 
 }  // namespace moe

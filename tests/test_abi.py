@@ -57,14 +57,14 @@ def test_workspace_queries(L):
     b = L.moe_forward_workspace_bytes(128, 256, 8, 2048, 512)
     R = 128 * 8
     assert b >= R * 2048 + R * 512 * 4 + 16 * 4 * R
-    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(16)]
+    offs = [L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(15)]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < b
     assert L.moe_forward_workspace_bytes(128, 256, 8, 2000, 512) == 0   # K % 128
-    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 16) == -1
-    fo = [L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, i) for i in range(14)]
+    assert L.moe_forward_workspace_offset(128, 256, 8, 2048, 512, 15) == -1
+    fo = [L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, i) for i in range(13)]
     assert fo == sorted(fo) and all(o % 256 == 0 for o in fo)
     assert fo[-1] < L.moe_ffn_workspace_bytes(64, 8, 2, 512, 256)
-    assert L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, 14) == -1
+    assert L.moe_ffn_workspace_offset(64, 8, 2, 512, 256, 13) == -1
     mo = [L.moe_mlp_workspace_offset(128, 256, 8, 2048, 512, i) for i in range(16)]
     mb = L.moe_mlp_workspace_bytes(128, 256, 8, 2048, 512)
     assert mo == sorted(mo) and all(o % 256 == 0 for o in mo) and mo[-1] < mb

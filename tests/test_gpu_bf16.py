@@ -277,13 +277,15 @@ def test_ffn_layer_mixtral_shape_chunk_edges(T):
                         flags=moe.MOE_FWD_SCHED(sched))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_np(out2, np.uint16), y)
-        q = ffn_ws_part(ws, T, E, k, H, F, 13, np.uint32, 2 * moe.MOE_QUEUE_WORDS)
+        q = ffn_ws_part(ws, T, E, k, H, F, 12, np.uint32, 2 * moe.MOE_QUEUE_WORDS)
         assert (q == 0).all()
     ids, _ = orc.route(logits, k, 30.0)
     counts, offsets = orc.layout(ids, E)
     np.testing.assert_array_equal(ffn_ws_part(ws, T, E, k, H, F, 2, np.int32, E), counts)
     np.testing.assert_array_equal(ffn_ws_part(ws, T, E, k, H, F, 3, np.int32, E + 1), offsets)
     srt = ffn_ws_part(ws, T, E, k, H, F, 8, np.int32, T * k)
+    # the layout's segments hold their routes in ascending route id: a stable sort by expert
+    np.testing.assert_array_equal(srt, np.argsort(ids.ravel(), kind="stable"))
     edges = chunk_edge_rows(counts)
     tok = np.unique(np.concatenate([srt[edges] // k,
                                     np.random.default_rng(1).choice(T, 32, replace=False)]))
