@@ -47,8 +47,9 @@ def parse():
     p.add_argument("--atomic-combine", action="store_true",
                    help="gathering path: the scatter-add combine (fp32 atomics into token rows, "
                         "then bf16) instead of fp32 routed rows and a gather-sum kernel")
-    p.add_argument("--fused-route", action="store_true",
-                   help="small-batch path: the route inside the grouped GEMM (two kernels)")
+    p.add_argument("--route-kernel", action="store_true",
+                   help="small-batch path: the route as a kernel of its own (three kernels) "
+                        "instead of inside the grouped GEMM (two, the default)")
     p.add_argument("--graph", action="store_true",
                    help="replay the cached HIP graph of the step instead of launching its kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -84,16 +85,19 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def gemm_algorithmic_bytes(counts, M, k, K, N, fused=False, gather=False):
+def gemm_algorithmic_bytes(counts, M, k, K, N, fused=False, gather=False, E=0):
     """Bytes the grouped GEMM must move: each non-empty expert's FP8 weights and scales once,
     the fp32 routed output rows once, and its inputs once: the routed FP8 rows, their scales
     and sorted ids (staged), the token-major FP8 rows, their scales and the sorted ids
     (gather), or the bf16 token rows and the routed ids (fused: layout, gather and
-    quantisation inside the GEMM)."""
+    quantisation inside the GEMM).  With E > 0 the route runs inside as well: the logits
+    [M][E] in place of the routed ids, and the ids and weights written."""
     nonempty = int((counts > 0).sum())
     R = M * k
     Nb, Kb = N // 128, K // 128
     weights = nonempty * (N * K + Nb * Kb * 4)
+    if fused and E:
+        return weights + M * K * 2 + M * E * 4 + R * N * 4 + R * 8
     if fused:
         acts = M * K * 2 + R * 4
     elif gather:
@@ -493,7 +497,7 @@ def bench_mlp(args, moe, synth, torch, np):
         "roofline": {"bound": "hbm", "kernel": gemm_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" ")[0]),
+                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" (")[0]),
                      "algorithmic_bytes_per_launch": gbytes,
                      "avg_launch_us": round(gemm_us, 3)},
     }
@@ -598,7 +602,7 @@ def main():
         (moe.MOE_FWD_GRAPH if args.graph else 0) | (moe.MOE_FWD_STAGED if args.staged else 0) | \
         (moe.MOE_FWD_SCHED(sched) if sched >= 0 else 0) | \
         (moe.MOE_FWD_ATOMIC_COMBINE if args.atomic_combine else 0) | \
-        (moe.MOE_FWD_FUSED_ROUTE if args.fused_route else 0)
+        (moe.MOE_FWD_ROUTE_KERNEL if args.route_kernel else 0)
 
     def step(i):
         moe.forward(logits, x, wqs[i % copies], wss[i % copies], k, cap, out, ws,
@@ -661,6 +665,17 @@ def main():
         def gemm(i):
             moe.grouped_gemm_gather(x_q, x_s, k, wqs[i % copies], wss[i % copies], tasks, ntasks,
                                     chunk, sorted_ids, rows_out, queue=queue, sched=sched)
+    elif nkern == 2:
+        # the step's first kernel alone: the route inside the grouped GEMM (its route words
+        # need no clearing between launches: each launch tags them anew)
+        ids_b = torch.empty((M, k), dtype=torch.int32, device=dev)
+        wts_b = torch.empty((M, k), dtype=torch.float32, device=dev)
+        words = torch.zeros(R, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def gemm(i):
+            moe.route_grouped_gemm(logits, x, k, cap, wqs[i % copies], wss[i % copies], ids_b,
+                                   wts_b, words, status, rows_out)
     elif fused:
         # the step's GEMM reads the routed ids (workspace part 0, written by its route stage)
         ids_ws = wsp(0, torch.int32, R).view(M, k)
@@ -684,14 +699,18 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     gemm_us = g0.elapsed_time(g1) * 1e3 / args.steps
-    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N, fused, gather)
+    gbytes = gemm_algorithmic_bytes(counts, M, k, K, N, fused, gather, E if nkern == 2 else 0)
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
 
     if gather:
         gemm_kernel = ("gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles gathered from "
                        "token-major rows, ROUTE_F32)")
+    elif nkern == 2:
+        gemm_kernel = ("gemm_fp8_fused_kernel<true, true> (the route inside the grouped FP8 GEMM "
+                       "from routed ids, rows at route ids)")
     elif fused:
-        gemm_kernel = "gemm_fp8_fused_kernel (grouped FP8 GEMM from routed ids, rows at route ids)"
+        gemm_kernel = ("gemm_fp8_fused_kernel<true, false> (grouped FP8 GEMM from routed ids, "
+                       "rows at route ids)")
     elif K in (512, 1024, 2048) and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
     elif 64 < chunk <= 256 and K <= 8192:
@@ -740,7 +759,7 @@ def main():
                      "kernel": gemm_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" ")[0]),
+                     "traffic": measured_traffic(args.workload, gemm_kernel.split(" (")[0]),
                      "algorithmic_bytes_per_launch": gbytes,
                      "avg_launch_us": round(gemm_us, 3)},
     }

@@ -50,10 +50,10 @@ typedef void* moe_stream_t; /* hipStream_t */
 /* Words of a grouped-GEMM task-counter buffer (`queue` arguments): per-XCD tickets, an exit
  * count and an error word.  Zero before first use; every launch leaves it zeroed. */
 #define MOE_QUEUE_WORDS 16
-/* Word of moe_forward's part 7 (the task counters) that the step sets to 1 when the
- * route-fused GEMM (MOE_FWD_FUSED_ROUTE) stopped waiting for the routed ids: that step's
- * output is then not valid.  It stays set until the caller clears it or a step that builds a
- * layout resets the counters. */
+/* Word of moe_forward's part 7 (the task counters) that the two-kernel small-batch step
+ * sets to 1 when a wave of its GEMM stopped waiting for a routing wave and routed tokens
+ * itself (informational: the output is complete and the same either way).  It stays set
+ * until the caller clears it or a step that builds a layout resets the counters. */
 #define MOE_QUEUE_HANDOFF_STATUS 10
 
 /* Task schedules of the LDS-tiled grouped GEMMs (BF16, and FP8 with chunks of 65..256 rows)
@@ -237,6 +237,22 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
  * MOE_SCHED_* value) picks how items reach workgroups, the queue forms counting in `queue`
  * (MOE_QUEUE_WORDS words, zero before the first call, left zeroed; NULL is allowed for
  * MOE_SCHED_DISPATCH and MOE_SCHED_STATIC). */
+/* ---- [FMF8] Baseline items 1-6 fused: the route inside the small-batch grouped GEMM ------
+ * moe_route and moe_grouped_gemm_routed in one launch (the first kernel of moe_forward's
+ * two-kernel step): logits f32 [M][E], x bf16 [M][K] -> topk_ids i32 and topk_weights f32
+ * [M][k] (as moe_route writes them) and rows f32 [M*k][N] at route ids (as
+ * moe_grouped_gemm_routed writes them).  Token t is routed by one wave of workgroup t % CUs,
+ * which publishes each route in route_words [M*k] (caller-owned scratch, any content at the
+ * call: a word left by an earlier call carries an older tag) as a tagged word; every
+ * workgroup polls the words it reads, and a wave still missing words after a bounded number
+ * of polls routes those tokens itself and sets *status to 1 (informational; the results are
+ * the same).  The words are left tagged.  Limits: those of moe_grouped_gemm_routed, and
+ * E <= 256, M at most 8 per CU, k <= 64; MOE_E_INVAL otherwise. */
+int moe_route_grouped_gemm(const float* logits, const uint16_t* x, int M, int E, int k, int K,
+                           float softcap, const uint8_t* w_q, const float* w_scales, int N,
+                           int32_t* topk_ids, float* topk_weights, uint32_t* route_words,
+                           uint32_t* status, float* rows, moe_stream_t stream);
+
 int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, int k, int K,
                             const uint8_t* w, const float* w_scales, int E, int N,
                             const moe_task* tasks, const int32_t* ntasks, int max_tasks,
@@ -296,15 +312,17 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
 #define MOE_FWD_STATIC_GRID 2
 /* bit 2: always run the five staged kernels (route, layout, moe_quant_sort_gather, grouped
  * GEMM, combine).  Without it:
- *  - a small batch (the limits of moe_grouped_gemm_routed, chunk_rows 16) runs three:
- *    route, the grouped GEMM straight from the routed ids (layout, sort/gather and
- *    quantisation inside it; fp32 rows at route ids), and the combine; the workspace then
- *    holds topk_ids, topk_weights and the GEMM rows (parts 0, 1 and 11) only;
- *  - chunk_rows in [65, 256] (K <= 8192) runs five: moe_route_quantize, the layout with the
- *    sorted route ids over many workgroups (a count kernel and a sort kernel), the
- *    moe_grouped_gemm_gather GEMM and the combine; the workspace then holds no a_q, a_scales
- *    or route_slots (parts 9, 10, 12) but the token-major x_q and x_scales (13, 14) and the
- *    sort's slot cursors (15). */
+ *  - a small batch (the limits of moe_grouped_gemm_routed, chunk_rows 16) runs the grouped
+ *    GEMM straight from the routed ids (layout, sort/gather and quantisation inside it; fp32
+ *    rows at route ids) and the combine, with the route inside that GEMM where E <= 256 and
+ *    M <= 8 per CU (two kernels, see bit 7), else as a kernel of its own before it (three);
+ *    the workspace then holds topk_ids, topk_weights and the GEMM rows (parts 0, 1 and 11),
+ *    and on the two-kernel path the route words in part 12;
+ *  - chunk_rows in [65, 256] (K <= 8192) runs four: moe_route_quantize, the layout with the
+ *    sorted route ids over many workgroups (one launch; each segment in ascending route id),
+ *    the moe_grouped_gemm_gather GEMM and the combine; the workspace then holds no a_q,
+ *    a_scales or route_slots (parts 9, 10, 12) but the token-major x_q and x_scales (13,
+ *    14). */
 #define MOE_FWD_STAGED 4
 /* bits 3-5: the task schedule of the tiled gathering GEMM, MOE_FWD_SCHED(MOE_SCHED_...);
  * 0 picks the default.  The queue forms use workspace part 7 as their counters. */
@@ -317,21 +335,27 @@ int moe_forward(const float* logits, const uint16_t* x, const uint8_t* w_q,
  * the gathering path (chunk_rows in [65, 256], K <= 8192, not STAGED) with hardware
  * dispatch. */
 #define MOE_FWD_ATOMIC_COMBINE 64
-/* bit 7: on the small-batch path with E <= 256 and at most 8 tokens per CU, run two kernels
- * instead of three: the route moves into the grouped GEMM ([FMF8] "Baseline: 7 kernels"
- * item 1 fused with items 2-6).  Token t is routed by one wave of workgroup t % CUs, which
- * writes topk_ids and topk_weights and publishes each route as a tagged word in part 12
- * (route_slots, unused on this path); every workgroup waits for the route words it reads (a
- * bounded wait, see MOE_QUEUE_HANDOFF_STATUS) and the combine clears them.  Same results as
- * without the bit.  Elsewhere the bit is ignored. */
-#define MOE_FWD_FUSED_ROUTE 128
+/* The small-batch path with E <= 256 and at most 8 tokens per CU runs two kernels by
+ * default: the route moves into the grouped GEMM ([FMF8] "Baseline: 7 kernels" item 1 fused
+ * with items 2-6).  Token t is routed by one wave of workgroup t % CUs, which writes topk_ids
+ * and topk_weights and publishes each route as a word tagged for this call in part 12
+ * (route_slots, unused on this path).  Every workgroup polls the route words it reads; a
+ * wave whose words are still missing after a bounded number of polls routes those tokens
+ * itself (see MOE_QUEUE_HANDOFF_STATUS), so the result never depends on another workgroup
+ * being resident.  The combine clears the words.  Same results as three kernels.
+ * bit 7: run the route as a kernel of its own instead (three kernels).
+ * bit 8: on the two-kernel path, route without the handoff: every wave routes the tokens it
+ * reads itself (the late-routing-wave fallback on every wave; slower, for tests). */
+#define MOE_FWD_ROUTE_KERNEL 128
+#define MOE_FWD_ROUTE_SELF 256
 int moe_forward_ex(const float* logits, const uint16_t* x, const uint8_t* w_q,
                    const float* w_scales, int M, int E, int k, int K, int N, float softcap,
                    uint16_t* out, void* workspace, size_t workspace_bytes, int chunk_rows,
                    int flags, moe_stream_t stream);
 
-/* Number of kernels moe_forward_ex launches for these arguments: 2 (small batch with
- * MOE_FWD_FUSED_ROUTE), 3 (small batch), 4 (the gathering path) or 5 (the staged one);
+/* Number of kernels moe_forward_ex launches for these arguments: 2 (small batch, route
+ * inside the GEMM), 3 (small batch with the route as a kernel), 4 (the gathering path) or 5
+ * (the staged one);
  * MOE_E_INVAL for arguments moe_forward_ex rejects. */
 int moe_forward_kernels(int M, int E, int k, int K, int N, int chunk_rows, int flags);
 

@@ -133,12 +133,13 @@ struct FwdArgs {
 };
 
 constexpr int kFwdFlagBits = MOE_FWD_GRAPH | MOE_FWD_STATIC_GRID | MOE_FWD_STAGED |
-                             MOE_FWD_SCHED_MASK | MOE_FWD_ATOMIC_COMBINE | MOE_FWD_FUSED_ROUTE;
+                             MOE_FWD_SCHED_MASK | MOE_FWD_ATOMIC_COMBINE |
+                             MOE_FWD_ROUTE_KERNEL | MOE_FWD_ROUTE_SELF;
 
 // Whether the step runs as two kernels: the small-batch GEMM with the route inside, then the
-// combine.
+// combine (the default wherever that GEMM can route).
 bool fwd_route_fused(int M, int E, int k, int K, int N, int chunk, int flags) {
-    return (flags & MOE_FWD_FUSED_ROUTE) && !(flags & MOE_FWD_STAGED) &&
+    return !(flags & (MOE_FWD_ROUTE_KERNEL | MOE_FWD_STAGED)) &&
            forward_fused_applies(M, k, E, K, N, chunk) && fused_route_applies(M, k, E);
 }
 bool fwd_flags_ok(int flags) {
@@ -211,7 +212,8 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         uint32_t* handoff = reinterpret_cast<uint32_t*>(slots);
         if ((e = launch_gemm_fp8_fused_route(a.logits, a.x, a.M, a.k, a.E, a.softcap, a.w_q,
                                              a.w_scales, a.N, ids, wts, handoff,
-                                             queue + MOE_QUEUE_HANDOFF_STATUS, rows, s)) !=
+                                             queue + MOE_QUEUE_HANDOFF_STATUS, rows,
+                                             (a.flags & MOE_FWD_ROUTE_SELF) != 0, s)) !=
             hipSuccess)
             return e;
         return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s, handoff,
@@ -579,6 +581,24 @@ int moe_grouped_gemm_routed(const uint16_t* x, const int32_t* topk_ids, int M, i
     hipError_t e = launch_gemm_fp8_fused(x, topk_ids, M, k, E, w_q, w_scales, N, rows, s);
     if (e == hipSuccess && counts) e = launch_counts(topk_ids, M, k, E, counts, offsets, s);
     return hip_status(e);
+}
+
+int moe_route_grouped_gemm(const float* logits, const uint16_t* x, int M, int E, int k, int K,
+                           float softcap, const uint8_t* w_q, const float* w_scales, int N,
+                           int32_t* topk_ids, float* topk_weights, uint32_t* route_words,
+                           uint32_t* status, float* rows, moe_stream_t stream) {
+    if (!route_dims_ok(M, E, k) || M < 1 || N < 128 || N % 128 || softcap != softcap)
+        return MOE_E_INVAL;
+    if (!logits || !x || !w_q || !w_scales || !topk_ids || !topk_weights || !route_words ||
+        !status || !rows)
+        return MOE_E_INVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    if (!forward_fused_applies(M, k, E, K, N, 16) || !fused_route_applies(M, k, E))
+        return MOE_E_INVAL;
+    return hip_status(launch_gemm_fp8_fused_route(logits, x, M, k, E, softcap, w_q, w_scales,
+                                                  N, topk_ids, topk_weights, route_words,
+                                                  status, rows, false, (hipStream_t)stream));
 }
 
 int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, int k, int K,

@@ -34,21 +34,24 @@
 //
 // Routing inside (the ROUTE form; [FMF8] "Baseline: 7 kernels" item 1 folded in as well).
 // Token t is routed by wave t / G of workgroup t % G (G workgroups) before that wave waits for
-// anything.  It writes the token's ids and weights for the combine, and each route once more
-// into the handoff words as kRouteTag | expert with an agent-scope store: a word carries its
-// own validity, so no flag, fence or ordering between stores is needed.  Every thread of
-// every workgroup polls its four route words (agent-scope loads, which also fetch the ids it
-// needs) until they carry the tag, at most kMaxPolls rounds.  No wait depends on a workgroup
-// that has not been dispatched: the routing waves wait for nothing first.  A workgroup whose
-// wait gives up sets *status and skips its slices (its rows are not written).  The handoff
-// words must not carry the tag when the kernel starts: the combine that follows clears them.
-// The tag's high half, 0x7FBA, makes a signalling-NaN pattern and a 0x7F byte, which no
-// kernel of this library stores (E4M3 codes never hold 0x7F, computed NaNs are the default
-// one, ids and counts are small), so neither old data nor an earlier step can pass for a
-// fresh route.
+// anything; its logits loads go out ahead of the CU's weight burst (a workgroup barrier right
+// after they are issued), since the CU serves its requests in order.  The wave writes the
+// token's ids and weights for the combine, and each route once more into the handoff words as
+// tag | expert with an agent-scope store: a word carries its own validity, so no flag, fence
+// or ordering between stores is needed.  Every thread of every workgroup polls its four route
+// words (agent-scope loads, which also fetch the ids it needs) until they carry this call's
+// tag, at most max_polls rounds; a wave whose words are still missing then routes those
+// tokens itself (the same selection, so the same experts) and sets *status, so no wait can
+// fail and no wait depends on a workgroup that has not been dispatched.  A word is
+// 0x7FA00000 | epoch << 8 | expert (a 12-bit epoch that changes with every call, an 8-bit
+// expert): as a float every such word is a signalling NaN (computed NaNs are the quiet
+// default, +-inf is 0x7F800000 / 0xFF800000), and its top byte 0x7F is a code the library's
+// E4M3 encoder never writes, so old bytes do not pass for a route, and a word left by an
+// earlier call carries an older epoch (the forward's combine also clears them).
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace moe {
@@ -65,8 +68,6 @@ constexpr int kMaxLocal = 4;                  // experts touched by one workgrou
 constexpr int kTiles = 4;                     // resident 16-row tiles
 constexpr int kXSteps = 256 / 4 / kWaves;     // x loads per lane for one tile
 constexpr int kRouteVPL = 4;                  // ROUTE form: logits per lane, E <= 256
-constexpr uint32_t kRouteTag = 0x7FBA0000u;   // high half of a published route word
-constexpr int kMaxPolls = 1 << 18;
 
 struct FusedLds {
     uint4 frag[kTiles][kKB * 2 * 64];         // fragment f = (k-block f/2, half f%2)
@@ -78,7 +79,6 @@ struct FusedLds {
     int trc[kTiles];                          // rows of each resident tile
     int tlb[kTiles];                          // list position of its row 0
     int wsum[2][kWaves];
-    int wave_ok[kWaves];                      // ROUTE form: the wave's routes all arrived
 };
 
 // Arguments of the ROUTE form (unused otherwise).
@@ -86,8 +86,10 @@ struct FusedRoute {
     const float* logits;                      // f32 [M][E]
     int32_t* ids;                             // out: topk_ids [M][k]
     float* weights;                           // out: topk_weights [M][k]
-    uint32_t* handoff;                        // [M*k] route words, no tag at launch
-    uint32_t* status;                         // set to 1 when a wait gives up
+    uint32_t* handoff;                        // [M*k] route words, without this call's tag
+    uint32_t* status;                         // set to 1 when a wave routed tokens itself
+    uint32_t tag;                             // 0x7FA00000 | epoch << 8
+    int max_polls;                            // poll rounds before a wave routes for itself
     int M, E;
     float softcap;
 };
@@ -132,15 +134,16 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     const int hi = (int)((long long)slices * (blockIdx.x + 1) / gridDim.x);
     if constexpr (ROUTE) {
         const int t = blockIdx.x + gridDim.x * wave;
+        float val[kRouteVPL];
+        if (t < rt.M) route_load_row<kRouteVPL>(rt.logits + (size_t)t * rt.E, rt.E, lane, val);
+        if (blockIdx.x < rt.M) barrier_lds();   // the logits go out ahead of the weight burst
         if (t < rt.M) {                         // wave-uniform: this wave routes token t
-            float val[kRouteVPL];
-            route_load_row<kRouteVPL>(rt.logits + (size_t)t * rt.E, rt.E, lane, val);
             int my_e;
             float my_w;
             route_select<kRouteVPL>(val, rt.E, k, rt.softcap, lane, my_e, my_w);
             if (lane < k) {
                 const size_t r = (size_t)t * k + lane;
-                __hip_atomic_store(rt.handoff + r, kRouteTag | (uint32_t)my_e,
+                __hip_atomic_store(rt.handoff + r, rt.tag | (uint32_t)my_e,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 rt.ids[r] = my_e;
                 rt.weights[r] = my_w;
@@ -178,7 +181,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     // ids goes a small first burst: the first kPre units of the wave's first slice of the
     // range (unless routing moves the wave's start, the slice it will stream first).  It keeps
     // the memory busy while the tiles are built, yet drains before the x rows are requested.
-    constexpr int kPre = 4;
+    constexpr int kPre = ROUTE ? 6 : 4;
     const int s_pre = min(lo + wave, hi - 1);
     int v[4];
     if constexpr (!ROUTE) {
@@ -201,36 +204,52 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
         }
         __builtin_amdgcn_sched_barrier(0);
         unsigned have = 0;                      // bit u: v[u] arrived
-        int ok = 0;
-        for (int it = 0; it < kMaxPolls; ++it) {
+        for (int it = 0; it < rt.max_polls; ++it) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 if (!(have >> u & 1u)) {
                     const uint32_t wd = __hip_atomic_load(rt.handoff + min(tid * 4 + u, R - 1),
                                                           __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT);
-                    if ((wd & 0xFFFF0000u) == kRouteTag) {
-                        v[u] = (int)(wd & 0xFFFFu);
+                    if ((wd & 0xFFFFFF00u) == rt.tag) {
+                        v[u] = (int)(wd & 0xFFu);
                         have |= 1u << u;
                     }
                 }
             }
-            if (__ballot(have != 15u) == 0) {
-                ok = 1;
-                break;
-            }
+            if (__ballot(have != 15u) == 0) break;
             __builtin_amdgcn_s_sleep(2);
         }
-        if (lane == 0) {
-            L.wave_ok[wave] = ok;
-            if (!ok)
+        // Words still missing (their routing wave is late): the wave routes those tokens
+        // itself, one token per round, the lowest lane's first missing word first, and every
+        // lane takes the experts of its words on that token.  Each round fills at least one
+        // word, so at most 256 rounds.
+        uint64_t need = __ballot(have != 15u);
+        if (need != 0) {
+            if (lane == 0)
                 __hip_atomic_store(rt.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        barrier_lds();
-        int all_ok = 1;
+            do {
+                const int src = __ffsll((unsigned long long)need) - 1;
+                const unsigned hs = __shfl(have, src);
+                const int rs = min((wave * 64 + src) * 4 + __ffs(~hs & 15u) - 1, R - 1);
+                const int ts = rs / k;
+                float val[kRouteVPL];
+                route_load_row<kRouteVPL>(rt.logits + (size_t)ts * rt.E, rt.E, lane, val);
+                int my_e;
+                float my_w;
+                route_select<kRouteVPL>(val, rt.E, k, rt.softcap, lane, my_e, my_w);
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) all_ok &= L.wave_ok[i];
-        if (!__builtin_amdgcn_readfirstlane(all_ok)) return;      // whole workgroup
+                for (int u = 0; u < 4; ++u) {
+                    const int j = min(tid * 4 + u, R - 1) - ts * k;   // word's place in token ts
+                    const int e_j = __shfl(my_e, j & 63);
+                    if (!(have >> u & 1u) && j >= 0 && j < k) {
+                        v[u] = e_j;
+                        have |= 1u << u;
+                    }
+                }
+                need = __ballot(have != 15u);
+            } while (need != 0);
+        }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)                 // local expert index; invalid ids match none
@@ -487,10 +506,15 @@ hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, i
                                        int E, float softcap, const uint8_t* w,
                                        const float* w_scales, int N, int32_t* ids,
                                        float* weights, uint32_t* handoff, uint32_t* status,
-                                       float* rows_out, hipStream_t s) {
+                                       float* rows_out, bool self_route, hipStream_t s) {
+    static std::atomic<uint32_t> epoch{0};
+    const uint32_t tag = 0x7FA00000u | ((epoch.fetch_add(1) & 0xFFFu) << 8);
+    // a routing wave normally publishes within a few microseconds; 4096 rounds of polls
+    // (milliseconds) only run out when its workgroup waits for a CU another kernel holds
+    const int max_polls = self_route ? 0 : 4096;
     const int grid = device_info().cu_count;    // every token's routing wave is in the grid
     const int slices = E * (N / 16);
-    const FusedRoute rt{logits, ids, weights, handoff, status, M, E, softcap};
+    const FusedRoute rt{logits, ids, weights, handoff, status, tag, max_polls, M, E, softcap};
     hipLaunchKernelGGL((gemm_fp8_fused_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s,
                        x, nullptr, M * k, k, w, w_scales, N, slices, rows_out, rt);
     return hipGetLastError();

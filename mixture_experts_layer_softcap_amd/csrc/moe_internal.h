@@ -130,7 +130,7 @@ hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, i
                                        int E, float softcap, const uint8_t* w,
                                        const float* w_scales, int N, int32_t* ids,
                                        float* weights, uint32_t* handoff, uint32_t* status,
-                                       float* rows_out, hipStream_t s);
+                                       float* rows_out, bool self_route, hipStream_t s);
 
 // per-expert counts [E] and exclusive offsets [E+1] of the routed ids (E <= 1024)
 hipError_t launch_counts(const int32_t* ids, int M, int k, int E, int32_t* counts,

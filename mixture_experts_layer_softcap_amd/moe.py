@@ -31,7 +31,8 @@ MOE_FWD_GRAPH = 1
 MOE_FWD_STATIC_GRID = 2
 MOE_FWD_STAGED = 4
 MOE_FWD_ATOMIC_COMBINE = 64
-MOE_FWD_FUSED_ROUTE = 128
+MOE_FWD_ROUTE_KERNEL = 128
+MOE_FWD_ROUTE_SELF = 256
 
 MOE_QUEUE_WORDS = 16
 MOE_QUEUE_HANDOFF_STATUS = 10
@@ -63,6 +64,8 @@ SIGNATURES = {
                               _P, _P, _I, _P]),
     "moe_forward_kernels": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_grouped_gemm_routed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
+    "moe_route_grouped_gemm": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _P, _P, _P,
+                                    _P]),
     "moe_grouped_gemm_gather": (_I, [_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P,
                                      _P, _I, _P]),
     "moe_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -211,6 +214,17 @@ def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
     if n < 0:
         raise MoeError("moe_forward_kernels", n)
     return n
+
+
+def route_grouped_gemm(logits, x, k: int, softcap: float, w_q, w_scales, topk_ids,
+                       topk_weights, route_words, status, rows, stream=None):
+    """The route inside the small-batch grouped FP8 GEMM (moe_route_grouped_gemm)."""
+    M, E = logits.shape
+    K = x.shape[1]
+    N = w_q.shape[1]
+    _call("moe_route_grouped_gemm", _ptr(logits), _ptr(x), M, E, k, K, softcap, _ptr(w_q),
+          _ptr(w_scales), N, _ptr(topk_ids), _ptr(topk_weights), _ptr(route_words),
+          _ptr(status), _ptr(rows), _stream(stream))
 
 
 def grouped_gemm_routed(x, topk_ids, E: int, w_q, w_scales, rows, counts=None, offsets=None,

@@ -127,7 +127,13 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws - 1, 0, 0, S) == NOSPC
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 64, S) == INVAL    # flags
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 5 << 3, S) == INVAL  # sched
-    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 256, S) == INVAL    # bit 8
+    assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 0, 512, S) == INVAL    # bit 9
+    rg = L.moe_route_grouped_gemm
+    assert rg(P, P, 128, 256, 8, 2048, 30.0, P, P, 512, P, P, NULL, P, P, S) == INVAL  # words
+    assert rg(P, P, 128, 256, 8, 2048, 30.0, P, P, 512, P, P, P, NULL, P, S) == INVAL  # status
+    assert rg(P, P, 128, 256, 8, 2048, float("nan"), P, P, 512, P, P, P, P, P, S) == INVAL
+    assert rg(P, P, 128, 256, 8, 2048, 30.0, P, P, 500, P, P, P, P, P, S) == INVAL  # N % 128
+    assert rg(P, P, 128, 8, 9, 2048, 30.0, P, P, 512, P, P, P, P, P, S) == INVAL    # k > E
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 256, moe.MOE_FWD_SCHED(2),
              S) == INVAL                                                       # 256 rows
     assert f(P, P, P, P, 8, 16, 2, 256, 256, 30.0, P, P, ws, 257, 0, S) == INVAL   # chunk

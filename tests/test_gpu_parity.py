@@ -751,7 +751,7 @@ def ws_part(ws, d, which, dtype, count):
 
 
 @pytest.mark.parametrize("flags", [0, moe.MOE_FWD_GRAPH, moe.MOE_FWD_STATIC_GRID,
-                                   moe.MOE_FWD_STAGED])
+                                   moe.MOE_FWD_STAGED, moe.MOE_FWD_ROUTE_KERNEL])
 @pytest.mark.parametrize("name", [TINY, QWEN])
 def test_forward_full(name, flags):
     d = workload(name)
@@ -895,7 +895,7 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
         assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N} chunk={chunk}")
 
 
-@pytest.mark.parametrize("graph", [False, True])
+@pytest.mark.parametrize("mode", ["handoff", "handoff_graph", "self"])
 @pytest.mark.parametrize("M,E,k,N", [
     (128, 256, 8, 512),     # the M=128, E=256, top-8 layer
     (1, 16, 1, 128),        # one token: one routing wave; 128 workgroups without slices exit
@@ -903,18 +903,22 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
     (300, 128, 4, 128),     # more tokens than workgroups: second waves route as well
     (2048, 128, 1, 128),    # every wave of every workgroup routes a token
 ])
-def test_forward_fused_route_matches_three_kernels(M, E, k, N, graph):
-    # the two-kernel step (route inside the small-batch GEMM, ids handed over through flags in
-    # the workspace) against the three-kernel step: the same ids, weights and output bits,
-    # call after call, starting from a workspace full of old bytes; the combine leaves the
-    # flags cleared and the handoff status zero
+def test_forward_fused_route_matches_three_kernels(M, E, k, N, mode):
+    # the two-kernel step (the default: route inside the small-batch GEMM, routes handed over
+    # through tagged words in the workspace) against the three-kernel step: the same ids,
+    # weights and output bits, call after call, starting from a workspace full of old bytes;
+    # the combine leaves the words cleared.  "self": no handoff, every wave routes the tokens
+    # it reads itself (the path a wave takes when its routing wave is late), which sets the
+    # handoff status word; the handoff leaves it untouched.
     K = 2048
     d = synth.fused_inputs(M, E, k, K, N, seed=M + 7 * E)
     d.update(M=M, E=E, k=k, K=K, N=N)
     d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
-    flags = moe.MOE_FWD_FUSED_ROUTE | (moe.MOE_FWD_GRAPH if graph else 0)
+    flags = {"handoff": 0, "handoff_graph": moe.MOE_FWD_GRAPH,
+             "self": moe.MOE_FWD_ROUTE_SELF}[mode]
     assert moe.forward_kernels(M, E, k, K, N, 0, flags) == 2
-    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True)
+    assert moe.forward_kernels(M, E, k, K, N, 0, flags | moe.MOE_FWD_ROUTE_KERNEL) == 3
+    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True, flags=moe.MOE_FWD_ROUTE_KERNEL)
     ws = zeros(moe.forward_workspace_bytes(M, E, k, K, N), torch.uint8)
     ws.fill_(0xA5)
     out = zeros((M, N), torch.int16)
@@ -928,16 +932,18 @@ def test_forward_fused_route_matches_three_kernels(M, E, k, N, graph):
         for part, dt in ((0, np.int32), (1, np.float32)):
             np.testing.assert_array_equal(ws_part(ws, d, part, dt, R), ws_part(ws3, d, part, dt, R))
         assert (ws_part(ws, d, 12, np.uint32, R) == 0).all(), "route words left set"
-        assert ws_part(ws, d, 7, np.uint32, moe.MOE_QUEUE_WORDS)[
-            moe.MOE_QUEUE_HANDOFF_STATUS] == 0xA5A5A5A5, "handoff status written"
+        status = ws_part(ws, d, 7, np.uint32, moe.MOE_QUEUE_WORDS)[moe.MOE_QUEUE_HANDOFF_STATUS]
+        assert status == (1 if mode == "self" else 0xA5A5A5A5), hex(status)
     ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
     assert_bf16_close(base[0], ref["y64"], f"fused route M={M} E={E} k={k} N={N}")
 
 
-def test_forward_fused_route_ties_and_non_finite_logits():
-    # the route inside the GEMM follows the route's order on crafted rows: all tied, ten tied
-    # above the rest (the k/k+1 boundary), NaN (below every number) and +inf logits; ids
-    # against the oracle's route, output bits against the three-kernel step
+@pytest.mark.parametrize("flags", [0, 256])
+def test_forward_fused_route_ties_and_non_finite_logits(flags):
+    # the route inside the GEMM (handed over, or taken by every wave itself: flags 256 =
+    # MOE_FWD_ROUTE_SELF) follows the route's order on crafted rows: all tied, ten tied above
+    # the rest (the k/k+1 boundary), NaN (below every number) and +inf logits; ids against the
+    # oracle's route, output bits against the three-kernel step
     M, E, k, K, N = 16, 64, 4, 2048, 128
     d = synth.fused_inputs(M, E, k, K, N, seed=5)
     lg = d["logits"]
@@ -949,10 +955,9 @@ def test_forward_fused_route_ties_and_non_finite_logits():
     lg[4, 60:] = np.inf
     d.update(M=M, E=E, k=k, K=K, N=N)
     d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
-    f = moe.MOE_FWD_FUSED_ROUTE
-    assert moe.forward_kernels(M, E, k, K, N, 0, f) == 2
-    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True)
-    (got, ws2) = gpu_forward(d, flags=f, reps=2, keep_ws=True)
+    assert moe.forward_kernels(M, E, k, K, N, 0, flags) == 2
+    (base, ws3) = gpu_forward(d, reps=1, keep_ws=True, flags=moe.MOE_FWD_ROUTE_KERNEL)
+    (got, ws2) = gpu_forward(d, flags=flags, reps=2, keep_ws=True)
     R = M * k
     r_ids, _ = orc.route(lg, k, CAP)
     np.testing.assert_array_equal(ws_part(ws2, d, 0, np.int32, R).reshape(M, k), r_ids)
@@ -962,12 +967,15 @@ def test_forward_fused_route_ties_and_non_finite_logits():
 
 
 def test_forward_fused_route_only_where_it_applies():
-    # E above 256 or a batch outside the small-batch path keeps the route kernel
-    f = moe.MOE_FWD_FUSED_ROUTE
-    assert moe.forward_kernels(100, 300, 3, 2048, 384, 0, f) == 3
-    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, f) == 5
-    assert moe.forward_kernels(1024, 256, 8, 2048, 512, 0, f) == 4
-    assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, f | moe.MOE_FWD_STAGED) == 5
+    # the route moves into the GEMM by default on the small-batch path with E <= 256; E above
+    # 256, a batch outside that path, the staged flag or MOE_FWD_ROUTE_KERNEL keep the route
+    # kernel
+    assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, 0) == 2
+    assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, moe.MOE_FWD_ROUTE_KERNEL) == 3
+    assert moe.forward_kernels(100, 300, 3, 2048, 384, 0, 0) == 3
+    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, 0) == 5
+    assert moe.forward_kernels(1024, 256, 8, 2048, 512, 0, 0) == 4
+    assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, moe.MOE_FWD_STAGED) == 5
 
 
 def test_forward_repeat_determinism():
