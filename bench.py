@@ -422,9 +422,21 @@ def bench_mlp(args, moe, synth, torch, np):
 
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if H <= 8192 else 64))
-    fused = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows) == 5
+    nkern = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows)
+    fused = nkern in (4, 5)
     h1 = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
-    if fused:
+    if nkern == 4:
+        # the gate+up GEMM alone with the route inside, as the step runs it
+        ids_b = torch.empty((M, k), dtype=torch.int32, device=dev)
+        wts_b = torch.empty((M, k), dtype=torch.float32, device=dev)
+        words = torch.zeros(R, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def gemm(i):
+            a = w1s[i % copies]
+            moe.route_grouped_gemm(logits, x, k, cap, a[0], a[1], ids_b, wts_b, words, status,
+                                   h1)
+    elif fused:
         # the gate+up GEMM alone, straight from the routed ids the last step left (part 0)
         ids_ws = wsp(0, torch.int32, R).view(M, k)
 
@@ -463,14 +475,17 @@ def bench_mlp(args, moe, synth, torch, np):
     counts = np.bincount(ids_np, minlength=E)
     nonempty = int((counts > 0).sum())
     N1 = 2 * I
-    acts = (M * H * 2 + R * 4) if fused else (R * H + (H // 128) * R * 4 + R * 4)
+    acts = (M * H * 2 + M * E * 4 + R * 8) if nkern == 4 else \
+        (M * H * 2 + R * 4) if fused else (R * H + (H // 128) * R * 4 + R * 4)
     gbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4) + acts + R * N1 * 4
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
     lbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4) \
         + M * E * 4 + M * H * 2 + M * H * 2
     flops = 2.0 * R * (N1 * H + H * I)
-    gemm_kernel = ("gemm_fp8_fused_kernel (gate+up grouped FP8 GEMM from routed ids, rows at "
-                   "route ids)" if fused else
+    gemm_kernel = ("gemm_fp8_fused_kernel<true, true> (the route inside the gate+up grouped "
+                   "FP8 GEMM from routed ids, rows at route ids)" if nkern == 4 else
+                   "gemm_fp8_fused_kernel<true, false> (gate+up grouped FP8 GEMM from routed "
+                   "ids, rows at route ids)" if fused else
                    "gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
                    if H == 2048 and chunk <= 16 else
                    "gemm_fp8_tile_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
@@ -484,7 +499,10 @@ def bench_mlp(args, moe, synth, torch, np):
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "H": H, "I": I,
                    "softcap": cap, "weight_copies_rotated": copies, "chunk_rows": chunk,
-                   "path": ("5 kernels: route, gate+up GEMM from the routed ids, layout (down "
+                   "path": ("4 kernels: gate+up GEMM routing its tokens itself, layout (down "
+                            "tasks, sorted ids) with silu*up requantise in one launch, down GEMM "
+                            "gathering by sorted id, combine" if nkern == 4 else
+                            "5 kernels: route, gate+up GEMM from the routed ids, layout (down "
                             "tasks, sorted ids) with silu*up requantise in one launch, down GEMM "
                             "gathering by sorted id, combine" if fused else
                             "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "

@@ -808,9 +808,9 @@ int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows) {
     if (rc) return rc;
     int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, H);
     if (!chunk_rows && chunk > 64 && Kmax > 8192) chunk = 64;
-    return forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)
-               ? 5
-               : 7;
+    if (!forward_fused_applies(M, k, E, H, 2 * I, chunk) || !gemm_fp8_range_applies(I, chunk))
+        return 7;
+    return fused_route_applies(M, k, E) ? 4 : 5;
 }
 
 int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
@@ -858,19 +858,28 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     hipError_t e;
     if (forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)) {
         // small batch: the gate+up GEMM straight from the routed ids (layout, gather and
-        // quantisation of x inside) with rows at route ids; the down projection's layout
-        // shares a launch with the activation step; the activations stay in route order and
-        // the down GEMM gathers its rows by sorted route id
-        if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) != hipSuccess ||
-            (e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s)) !=
-                hipSuccess ||
+        // quantisation of x inside; the route too where it can, handing the routes over
+        // through tagged words in the unused route_slots part) with rows at route ids; the
+        // down projection's layout shares a launch with the activation step; the activations
+        // stay in route order and the down GEMM gathers its rows by sorted route id
+        uint32_t* handoff = nullptr;
+        if (fused_route_applies(M, k, E)) {
+            handoff = reinterpret_cast<uint32_t*>(slots);
+            e = launch_gemm_fp8_fused_route(logits, x, M, k, E, softcap, w1_q, w1_scales, 2 * I,
+                                            ids, wts, handoff, queue + MOE_QUEUE_HANDOFF_STATUS,
+                                            h1, false, s);
+        } else if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) == hipSuccess) {
+            e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s);
+        }
+        if (e != hipSuccess ||
             (e = launch_layout_swiglu(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td,
                                       nt + 1, queue2, sorted, h1, I, aq, as, s)) !=
                 hipSuccess ||
             (e = launch_gemm_fp8_range(aq, as, R, I, w2_q, w2_scales, H, td, nt + 1, mtd,
                                        MOE_EPI_ROUTE_F32, sorted, h2, s, sorted)) !=
                 hipSuccess ||
-            (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s)) != hipSuccess)
+            (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s, handoff,
+                                handoff ? R : 0)) != hipSuccess)
             return hip_status(e);
         return MOE_OK;
     }

@@ -145,9 +145,9 @@ def ws_part(ws, d, which, dtype, n):
 @pytest.mark.parametrize("M,E,k,H,I,chunk,kernels", [
     (8, 16, 2, 256, 256, 0, 7),       # the correctness-sized layer; general GEMM for both
     (37, 5, 3, 384, 384, 64, 7),      # ragged segments, 64-row chunks
-    (64, 8, 2, 2048, 512, 16, 5),     # small batch: gate+up from the routed ids, layout and
-                                      # activations in one launch, down GEMM gathering its
-                                      # rows by sorted route id
+    (64, 8, 2, 2048, 512, 16, 4),     # small batch: gate+up from the routed ids with the
+                                      # route inside, layout and activations in one launch,
+                                      # down GEMM gathering its rows by sorted route id
     (64, 8, 2, 2048, 512, 128, 7),    # LDS-tiled GEMM for both projections
 ])
 def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
@@ -185,7 +185,7 @@ def test_mlp_forward_full_size():
     d = synth.mlp_inputs(**{kk: v for kk, v in
                             synth.MLP_WORKLOADS["mlp_fp8_M128_E256_k8_H2048_I512"].items()})
     M, E, k, H, I = d["M"], d["E"], d["k"], d["H"], d["I"]
-    assert moe.mlp_forward_kernels(M, E, k, H, I) == 5
+    assert moe.mlp_forward_kernels(M, E, k, H, I) == 4
     outs, ws = gpu_mlp(d, reps=2)
     np.testing.assert_array_equal(outs[1], outs[0])
     toks = np.arange(M, dtype=np.int32)
