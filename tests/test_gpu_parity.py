@@ -841,6 +841,28 @@ def test_forward_atomic_combine_only_on_the_gathering_path():
         gpu_forward(d, flags=moe.MOE_FWD_ATOMIC_COMBINE)
 
 
+@pytest.mark.parametrize("M,E,k", [(700, 1024, 3), (1500, 1000, 2), (345, 64, 8)])
+def test_forward_wide_layout_edges(M, E, k):
+    # the layout over many workgroups at its limits: up to 1024 experts (11-bit ballot match,
+    # a 16 x 1024 table of wave counts), route counts that leave the last 1024-route chunk
+    # ragged, and many empty experts; counts, offsets and the sorted route ids equal the
+    # oracle's exactly, and the whole output passes the oracle's bar
+    K, N = 256, 128
+    d = synth.fused_inputs(M, E, k, K, N, seed=M + E)
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    assert moe.forward_kernels(M, E, k, K, N, 128) == 4
+    outs, ws = gpu_forward(d, chunk=128, reps=2, keep_ws=True)
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP, intermediates=True)
+    R = M * k
+    np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, E), ref["counts"])
+    np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), ref["offsets"])
+    np.testing.assert_array_equal(ws_part(ws, d, 8, np.int32, R), ref["sorted_route_ids"])
+    for o in outs:
+        assert_bf16_close(o, ref["y64"], f"wide layout M={M} E={E} k={k}")
+        np.testing.assert_array_equal(o, outs[0])
+
+
 @pytest.mark.parametrize("name", [ZIPF1K, ZIPF4K])
 def test_forward_skewed_layout_repeats(name):
     # across repeated forwards the integer outputs (ids, counts, offsets, the set of tasks,
