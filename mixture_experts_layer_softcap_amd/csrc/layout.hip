@@ -291,7 +291,16 @@ __global__ __launch_bounds__(kThreads) void layout_wide_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int cb = blockIdx.x * kThreads;         // the chunk's first route
     const int r = cb + tid;
+    // this route's id and the first batch of the whole-batch histogram's ids go out together,
+    // ahead of the LDS clearing (kU loads in flight per thread ahead of their LDS atomics)
+    constexpr int kU = 8;
     const int e = r < R ? ids[r] : -1;
+    int q[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int rr = u * kThreads + tid;
+        q[u] = rr < R ? ids[rr] : -1;
+    }
     s_all[tid] = 0;
     s_before[tid] = 0;
     s_hist[tid] = 0;
@@ -311,21 +320,21 @@ __global__ __launch_bounds__(kThreads) void layout_wide_kernel(
     const int rank_w = __popcll(same & ((1ull << lane) - 1ull));
     if (v < E && rank_w == 0) s_wcnt[wave * E + v] = __popcll(same);
 
-    // histograms of the whole batch and of the routes before this chunk (four loads in flight
-    // per thread ahead of their LDS atomics)
-    for (int r0 = 0; r0 < R; r0 += 4 * kThreads) {
-        int q[4];
+    // histograms of the whole batch and of the routes before this chunk
+    for (int r0 = 0;;) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rr = r0 + u * kThreads + tid;
-            q[u] = rr < R ? ids[rr] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kU; ++u) {
             if ((unsigned)q[u] < (unsigned)E) {
                 atomicAdd(&s_all[q[u]], 1);
                 if (r0 + u * kThreads + tid < cb) atomicAdd(&s_before[q[u]], 1);
             }
+        }
+        r0 += kU * kThreads;
+        if (r0 >= R) break;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int rr = r0 + u * kThreads + tid;
+            q[u] = rr < R ? ids[rr] : -1;
         }
     }
     __syncthreads();
