@@ -246,8 +246,11 @@ int moe_grouped_gemm(int mode, const void* a, const float* a_scales, int rows, i
  * call: a word left by an earlier call carries an older tag) as a tagged word; every
  * workgroup polls the words it reads, and a wave still missing words after a bounded number
  * of polls routes those tokens itself and sets *status to 1 (informational; the results are
- * the same).  The words are left tagged.  Limits: those of moe_grouped_gemm_routed, and
- * E <= 256, M at most 8 per CU, k <= 64; MOE_E_INVAL otherwise. */
+ * the same).  The words are left tagged.  The tag changes with every call made through this
+ * function, but a launch captured in a HIP graph replays with the tag it was captured with:
+ * zero route_words between replays (moe_forward's combine does this for its own words).
+ * Limits: those of moe_grouped_gemm_routed, and E <= 256, M at most 8 per CU, k <= 64;
+ * MOE_E_INVAL otherwise. */
 int moe_route_grouped_gemm(const float* logits, const uint16_t* x, int M, int E, int k, int K,
                            float softcap, const uint8_t* w_q, const float* w_scales, int N,
                            int32_t* topk_ids, float* topk_weights, uint32_t* route_words,
