@@ -275,12 +275,80 @@ __global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restr
 // wave ballots find the lanes holding the same id, and the per-wave counts are prefixed in
 // wave order.  Every segment therefore holds its routes in ascending route id, the order of
 // the serial counting sort ([FMF8] Baseline item 5).
-__global__ __launch_bounds__(kThreads) void layout_wide_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
-    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue,
-    int32_t* __restrict__ sorted_route_ids, int32_t* __restrict__ route_slots, int n_blocks2,
-    moe_task* __restrict__ tasks2, int32_t* __restrict__ ntasks2, uint32_t* __restrict__ queue2) {
+
+struct WideLayoutOut {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* cursors;
+    moe_task* tasks;
+    int32_t* ntasks;
+    uint32_t* queue;
+    int32_t* sorted_route_ids;
+    int32_t* route_slots;                         // may be null
+    int n_blocks, chunk;
+    moe_task* tasks2;                             // a second task list, or null
+    int32_t* ntasks2;
+    uint32_t* queue2;
+    int n_blocks2;
+};
+
+// Everything after the histograms: route r of this chunk has id e; s_all and s_before hold
+// the whole batch's and the earlier chunks' counts (their atomics issued before the call),
+// s_wcnt [kWaves][E] is zero, s_hist zero; `writer`: this workgroup writes counts, offsets,
+// cursors and the task lists.
+__device__ __forceinline__ void wide_place(int e, int r, int R, int E, bool writer,
+                                           const WideLayoutOut& o, int* s_all, int* s_before,
+                                           int* s_first, int* s_hist, int* s_wsum,
+                                           int* s_wcnt) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // stable rank inside the wave: lanes whose value v (E for a route past R or an invalid id)
+    // agrees with this lane's in every bit
+    const int v = (unsigned)e < (unsigned)E ? e : E;
+    const int nbits = 32 - __clz(E);
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (v >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+    }
+    const int rank_w = __popcll(same & ((1ull << lane) - 1ull));
+    if (v < E && rank_w == 0) s_wcnt[wave * E + v] = __popcll(same);
+    __syncthreads();
+    if (tid < E) {                                // prefix of the wave counts, in wave order
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int t = s_wcnt[w * E + tid];
+            s_wcnt[w * E + tid] = run;
+            run += t;
+        }
+    }
+    const int c = tid < E ? s_all[tid] : 0;
+    int total_rows;
+    const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
+    if (tid < E) s_first[tid] = row0 + s_before[tid];
+    if (writer) {
+        if (tid < E) o.counts[tid] = c;
+        write_tasks(c, row0, E, o.n_blocks, o.chunk, o.offsets, o.cursors, o.tasks, o.ntasks,
+                    o.queue, s_hist, s_wsum);
+        if (o.tasks2) {                           // a second list over the same chunks
+            __syncthreads();
+            s_hist[tid] = 0;
+            __syncthreads();
+            write_tasks(c, row0, E, o.n_blocks2, o.chunk, o.offsets, o.cursors, o.tasks2,
+                        o.ntasks2, o.queue2, s_hist, s_wsum);
+        }
+    }
+    __syncthreads();
+    if (r < R) {
+        const int slot = v < E ? s_first[v] + s_wcnt[wave * E + v] + rank_w : -1;
+        if (slot >= 0) o.sorted_route_ids[slot] = r;
+        if (o.route_slots) o.route_slots[r] = slot;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void layout_wide_kernel(const int32_t* __restrict__ ids,
+                                                               int R, int E, WideLayoutOut o) {
     __shared__ int s_all[kThreads];               // routes per expert, whole batch
     __shared__ int s_before[kThreads];            // routes per expert in the chunks before this one
     __shared__ int s_first[kThreads];             // this chunk's first slot in each segment
@@ -288,7 +356,6 @@ __global__ __launch_bounds__(kThreads) void layout_wide_kernel(
     __shared__ int s_wsum[kWaves + 1];
     __shared__ int s_wcnt[kWaves * kThreads];     // [wave][expert]: count, then wave prefix
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
     const int cb = blockIdx.x * kThreads;         // the chunk's first route
     const int r = cb + tid;
     // this route's id and the first batch of the whole-batch histogram's ids go out together,
@@ -306,20 +373,6 @@ __global__ __launch_bounds__(kThreads) void layout_wide_kernel(
     s_hist[tid] = 0;
     for (int i = tid; i < kWaves * E; i += kThreads) s_wcnt[i] = 0;
     __syncthreads();
-
-    // stable rank inside the wave: lanes whose value v (E for a route past R or an invalid id)
-    // agrees with this lane's in every bit
-    const int v = (unsigned)e < (unsigned)E ? e : E;
-    const int nbits = 32 - __clz(E);
-    uint64_t same = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (v >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        same &= bit ? m : ~m;
-    }
-    const int rank_w = __popcll(same & ((1ull << lane) - 1ull));
-    if (v < E && rank_w == 0) s_wcnt[wave * E + v] = __popcll(same);
-
     // histograms of the whole batch and of the routes before this chunk
     for (int r0 = 0;;) {
 #pragma unroll
@@ -337,37 +390,8 @@ __global__ __launch_bounds__(kThreads) void layout_wide_kernel(
             q[u] = rr < R ? ids[rr] : -1;
         }
     }
-    __syncthreads();
-    if (tid < E) {                                // prefix of the wave counts, in wave order
-        int run = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            const int t = s_wcnt[w * E + tid];
-            s_wcnt[w * E + tid] = run;
-            run += t;
-        }
-    }
-    const int c = tid < E ? s_all[tid] : 0;
-    int total_rows;
-    const int row0 = block_exclusive_scan(c, s_wsum, total_rows);
-    if (tid < E) s_first[tid] = row0 + s_before[tid];
-    if (blockIdx.x == 0) {
-        if (tid < E) counts[tid] = c;
-        write_tasks(c, row0, E, n_blocks, chunk, offsets, cursors, tasks, ntasks, queue, s_hist,
-                    s_wsum);
-        if (tasks2) {                             // a second list over the same chunks
-            __syncthreads();
-            s_hist[tid] = 0;
-            __syncthreads();
-            write_tasks(c, row0, E, n_blocks2, chunk, offsets, cursors, tasks2, ntasks2, queue2,
-                        s_hist, s_wsum);
-        }
-    }
-    __syncthreads();
-    if (r < R) {
-        const int slot = v < E ? s_first[v] + s_wcnt[wave * E + v] + rank_w : -1;
-        if (slot >= 0) sorted_route_ids[slot] = r;
-        if (route_slots) route_slots[r] = slot;
-    }
+    wide_place(e, r, R, E, blockIdx.x == 0, o, s_all, s_before, s_first, s_hist, s_wsum,
+               s_wcnt);
 }
 
 }  // namespace
@@ -416,9 +440,9 @@ hipError_t launch_layout_sorted_wide(const int32_t* ids, int M, int k, int E, in
     const int R = M * k;
     if (R == 0) return hipSuccess;
     const unsigned grid = (unsigned)((R + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(layout_wide_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
-                       n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
-                       sorted_route_ids, route_slots, n_blocks2, tasks2, ntasks2, queue2);
+    const WideLayoutOut o{counts,  offsets, cursors,   tasks,      ntasks,  queue,  sorted_route_ids,
+                          route_slots, n_blocks, chunk_rows, tasks2, ntasks2, queue2, n_blocks2};
+    hipLaunchKernelGGL(layout_wide_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E, o);
     return hipGetLastError();
 }
 

@@ -235,6 +235,36 @@ __device__ __forceinline__ Quant8 quantise8(uint4 raw, bool valid) {
     return quantise8_f32(v, valid);
 }
 
+// Token t's values [k_lo, k_hi) of x bf16 [M][K] (whole 128-value blocks) quantised by one
+// wave with the rule of the QSG stage into token-major codes x_q [M][K] and scales
+// x_scales [K/128][M].  512 values per pass: lane l holds values [8l, 8l+8) of the pass, so a
+// 128-value block is an aligned group of 16 lanes, wholly inside or outside the slice.
+__device__ __forceinline__ void quantise_token_slice(const uint16_t* __restrict__ x, int M,
+                                                     int K, int t, int k_lo, int k_hi,
+                                                     uint8_t* __restrict__ x_q,
+                                                     float* __restrict__ x_scales, int lane) {
+    constexpr int kPasses = 2;
+    for (int base = k_lo; base < k_hi; base += kPasses * 512) {
+        uint4 xr[kPasses];
+#pragma unroll
+        for (int q = 0; q < kPasses; ++q) {
+            const int k0 = base + q * 512 + lane * 8;
+            xr[q] = make_uint4(0u, 0u, 0u, 0u);
+            if (k0 < k_hi) xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0);
+        }
+#pragma unroll
+        for (int q = 0; q < kPasses; ++q) {
+            const int k0 = base + q * 512 + lane * 8;
+            const bool valid = k0 < k_hi;
+            const Quant8 qv = quantise8(xr[q], valid);
+            if (valid) {
+                *reinterpret_cast<uint2*>(x_q + (size_t)t * K + k0) = qv.codes;
+                if ((lane & 15) == 0) x_scales[(size_t)(k0 >> 7) * M + t] = qv.scale;
+            }
+        }
+    }
+}
+
 // ---- matrix-core operands and vector-memory ordering ----
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -37,9 +37,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (QUANT && blockIdx.y > 0) {
-        // quantisation of token t's slice blockIdx.y - 1 of K (whole 128-value blocks); 512
-        // values per pass: lane l holds values [8l, 8l+8) of the pass, so a 128-value block
-        // is an aligned group of 16 lanes, wholly inside or outside the slice
+        // quantisation of token t's slice blockIdx.y - 1 of K
         if (t >= M) return;
         if (acc && blockIdx.y == 1) {
             // the token's fp32 accumulator row that the grouped GEMM adds its routes into
@@ -49,27 +47,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(
         }
         const int per = (K / 128 + kQuantSplit - 1) / kQuantSplit * 128;
         const int k_lo = (blockIdx.y - 1) * per;
-        const int k_hi = min(K, k_lo + per);
-        constexpr int kPasses = 2;
-        for (int base = k_lo; base < k_hi; base += kPasses * 512) {
-            uint4 xr[kPasses];
-#pragma unroll
-            for (int q = 0; q < kPasses; ++q) {
-                const int k0 = base + q * 512 + lane * 8;
-                xr[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (k0 < k_hi) xr[q] = *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0);
-            }
-#pragma unroll
-            for (int q = 0; q < kPasses; ++q) {
-                const int k0 = base + q * 512 + lane * 8;
-                const bool valid = k0 < k_hi;
-                const Quant8 qv = quantise8(xr[q], valid);
-                if (valid) {
-                    *reinterpret_cast<uint2*>(x_q + (size_t)t * K + k0) = qv.codes;
-                    if ((lane & 15) == 0) x_scales[(size_t)(k0 >> 7) * M + t] = qv.scale;
-                }
-            }
-        }
+        quantise_token_slice(x, M, K, t, k_lo, min(K, k_lo + per), x_q, x_scales, lane);
         return;
     }
     if (t >= M) return;
