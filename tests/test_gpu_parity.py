@@ -917,6 +917,42 @@ def test_forward_edge_shapes(M, E, k, K, N, bias):
         assert_bf16_close(y, ref["y64"], f"edge M={M} E={E} k={k} K={K} N={N} chunk={chunk}")
 
 
+def random_layer_shapes(n=24, seed=2026):
+    """Seeded layer shapes (M, E, k, K, N) spread over every path the forward can take: one
+    to several hundred tokens, one to a few hundred experts, k up to E, K a multiple of 128
+    (half of them 2048, the small-batch GEMM's depth) and one to four 128-column panels;
+    shapes whose oracle or weight quantisation would take more than about a second are
+    drawn again."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        M = int(np.exp(g.uniform(0, np.log(700))))
+        E = int(np.exp(g.uniform(0, np.log(400))))
+        k = int(g.integers(1, min(E, 10) + 1))
+        K = 2048 if g.random() < 0.5 else 128 * int(g.integers(1, 17))
+        N = 128 * int(g.integers(1, 5))
+        if E * N * K > 48 * 2 ** 20 or M * k * K * N > 1.2e9:
+            continue
+        shapes.append((M, E, k, K, N))
+    return shapes
+
+
+@pytest.mark.parametrize("M,E,k,K,N", random_layer_shapes())
+def test_forward_random_shapes(M, E, k, K, N):
+    # whole output against the oracle on seeded shapes that no hand-picked case names
+    # (E = 1, k = E, a token or two, hundreds of routes per expert, ragged K), in the default
+    # launch form and in the staged one
+    d = synth.fused_inputs(M, E, k, K, N, seed=M * 1009 + E * 31 + k * 7 + K + N)
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
+    for flags in (0, moe.MOE_FWD_STAGED):
+        n = moe.forward_kernels(M, E, k, K, N, 0, flags)
+        print(f"shape M={M} E={E} k={k} K={K} N={N} flags={flags}: {n} kernels", flush=True)
+        y = gpu_forward(d, flags=flags)[0]
+        assert_bf16_close(y, ref["y64"], f"M={M} E={E} k={k} K={K} N={N} flags={flags}")
+
+
 @pytest.mark.parametrize("mode", ["handoff", "handoff_graph", "self"])
 @pytest.mark.parametrize("M,E,k,N", [
     (128, 256, 8, 512),     # the M=128, E=256, top-8 layer
