@@ -253,6 +253,37 @@ def test_ffn_layer_small_full(chunk):
     assert_bf16_close(y, ref, f"ffn chunk={chunk}")
 
 
+def random_ffn_shapes(n=10, seed=2027):
+    """Seeded FFN layer shapes (T, E, k, H, F, chunk): one token to several hundred, one to 24
+    experts, k up to min(E, 4), hidden and FFN widths of one to four tiles, chunk 0 (the
+    default) or 64 / 128 / 256 rows; shapes whose oracle would take more than about a second
+    are drawn again."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        T = int(np.exp(g.uniform(0, np.log(600))))
+        E = int(g.integers(1, 25))
+        k = int(g.integers(1, min(E, 4) + 1))
+        H = 256 * int(g.integers(1, 5))
+        F = 128 * int(g.integers(1, 5))
+        chunk = int(g.choice([0, 64, 128, 256]))
+        if T * k * 3 * F * H > 6e8:
+            continue
+        shapes.append((T, E, k, H, F, chunk))
+    return shapes
+
+
+@pytest.mark.parametrize("T,E,k,H,F,chunk", random_ffn_shapes())
+def test_ffn_layer_random_shapes(T, E, k, H, F, chunk):
+    # whole layer against the oracle on seeded shapes no hand-picked case names (one expert,
+    # k = E, a single token, ragged last chunks at every chunk size)
+    d = synth.ffn_inputs(T, E, H, F, seed=T * 131 + E * 17 + k + H + F)
+    print(f"ffn T={T} E={E} k={k} H={H} F={F} chunk={chunk}", flush=True)
+    y = run_ffn(d, k, chunk)
+    _, ref = orc.ffn_tokens(d["logits"], d["x"], d["w_up"], d["w_down"], k, 30.0)
+    assert_bf16_close(y, ref, f"ffn T={T} E={E} k={k} H={H} F={F} chunk={chunk}")
+
+
 def ffn_ws_part(ws, T, E, k, H, F, which, dtype, n):
     off = moe.ffn_workspace_offset(T, E, k, H, F, which)
     return to_np(ws[off:off + n * np.dtype(dtype).itemsize]).view(dtype)
