@@ -165,6 +165,51 @@ def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
     np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), offsets)
 
 
+def random_mlp_shapes(n=10, seed=2028):
+    """Seeded MLP layer shapes (M, E, k, H, I, chunk): 8 to a few hundred tokens, one to 40
+    experts, k up to min(E, 8), hidden width 2048 (the small-batch path's depth) or one to
+    eight 128-column tiles, expert width one to eight tiles, chunk 0 (the default) or 16 / 64
+    / 128 rows; every third shape in the small-batch regime; at least 2048 output elements, so that the share of elements the per-element
+    bar lets through is a share of many; shapes whose oracle would take more than about a
+    second are drawn again."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        if len(shapes) % 3 == 2:
+            # the small-batch regime: hidden 2048, expert width 512 or 1024, at most 16
+            # routes per expert on average
+            E = int(g.integers(8, 65))
+            k = int(g.integers(1, 9))
+            M = int(g.integers(1, 16 * E // k + 1))
+            H, I, chunk = 2048, 512 * int(g.integers(1, 3)), int(g.choice([0, 16]))
+        else:
+            M = int(np.exp(g.uniform(np.log(8), np.log(400))))
+            E = int(g.integers(1, 41))
+            k = int(g.integers(1, min(E, 8) + 1))
+            H = 2048 if g.random() < 0.4 else 128 * int(g.integers(1, 9))
+            I = 128 * int(g.integers(1, 9))
+            chunk = int(g.choice([0, 16, 64, 128]))
+        if M * H < 2048 or M * k * 3 * I * H > 6e8:
+            continue
+        shapes.append((M, E, k, H, I, chunk))
+    return shapes
+
+
+@pytest.mark.parametrize("M,E,k,H,I,chunk", random_mlp_shapes())
+def test_mlp_forward_random_shapes(M, E, k, H, I, chunk):
+    # whole layer against the oracle on seeded shapes no hand-picked case names (one expert,
+    # k = E, ragged widths, every chunk size), in whichever launch form the shape takes; the
+    # kernels are deterministic, so a repeated call gives the same bits
+    d = synth.mlp_inputs(M, E, k, H, I, seed=M * 131 + E * 17 + k + H + I)
+    n = moe.mlp_forward_kernels(M, E, k, H, I, chunk)
+    print(f"mlp M={M} E={E} k={k} H={H} I={I} chunk={chunk}: {n} kernels", flush=True)
+    outs, _ = gpu_mlp(d, chunk=chunk, reps=2)
+    np.testing.assert_array_equal(outs[1], outs[0])
+    _, y64 = orc.mlp_tokens(d["logits"], d["x"], d["w1_q"], d["w1_s"], d["w2_q"], d["w2_s"],
+                            k, CAP)
+    assert_mlp_close(outs[0], y64, f"mlp M={M} E={E} k={k} H={H} I={I} chunk={chunk}")
+
+
 def e4m3_rank(codes):
     """Position of an E4M3FN code on the number line (codes of one sign are monotone in their
     low 7 bits; -0 and +0 share rank 0), so one rounding step apart is a rank difference 1."""
