@@ -65,8 +65,8 @@ typedef void* moe_stream_t; /* hipStream_t */
  *   MOE_SCHED_QUEUE      one workgroup per CU pulling tasks from one atomic counter
  *   MOE_SCHED_QUEUE_XCD  one workgroup per CU pulling from its XCD's own counter over that
  *                        XCD's run of tasks, then from the other XCDs' counters
- * The queue forms need a MOE_QUEUE_WORDS counter buffer.  MOE_SCHED_AUTO picks the measured
- * fastest for the shape. */
+ * The queue forms need a MOE_QUEUE_WORDS counter buffer.  MOE_SCHED_AUTO is hardware
+ * dispatch: on every workload measured it was the fastest or within noise of the fastest. */
 #define MOE_SCHED_AUTO (-1)
 #define MOE_SCHED_DISPATCH 0
 #define MOE_SCHED_STATIC 1
