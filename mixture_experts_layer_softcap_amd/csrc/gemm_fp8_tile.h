@@ -122,7 +122,8 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
     constexpr int S = Cfg::kStages;
     constexpr bool PERSIST = SCHED != MOE_SCHED_DISPATCH;
     __shared__ TileStage<BM> st0, st1, st2;     // st2 is used only with three stages
-    __shared__ float s_sw[2][kMaxKB];         // scales of the two weight panels per k-block
+    __shared__ float s_sw[kWaves][kMaxKB];    // rows 0, 1: scales of the two weight panels
+    __shared__ int s_ids[kWaves * 64];        // GATHER: sorted route ids of the chunk rows
     __shared__ int s_item[2];                 // tickets published to the workgroup
     auto stage = [&](auto bt) __attribute__((always_inline)) -> TileStage<BM>& {
         constexpr int Bi = decltype(bt)::value;
@@ -146,18 +147,33 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
     auto run_tile = [&](int task, int nb0, int np) __attribute__((always_inline)) {
         const int4 td = tasks[task];
         const int e = td.x, rb = td.y, rc = td.z;     // td.w == nb0
-        // weight-panel scales of every k-block (published by the first barrier)
-        for (int i = tid; i < np * KB; i += kThreads) {
-            const int pp = i >= KB, kb = i - pp * KB;
-            s_sw[pp][kb] = w_scales[((size_t)e * Nb + nb0 + pp) * KB + kb];
-        }
 
+        // Start-up order.  A CU serves its memory requests in order and a wait covers every
+        // older request, so nothing waits before the first stages' weight DMAs, which need
+        // only the task: the weight-panel scales and the gathered rows' sorted route ids go
+        // straight into LDS (the oldest requests), then the weights of stages 0 and 1 go out,
+        // and the row DMAs follow once the ids are in.  Everything in flight is LDS DMA: with
+        // plain loads into registers pending beside LDS DMAs the compiler can no longer count
+        // which has landed and waits for all of them.
+        //
         // DMA sources.  Weight rows: wave w moves slab rows [32w, 32w+32) (4 instructions of
         // 8 rows; a slab with one panel repeats it).  A rows: 8-row group w + 8i (i < BM/64)
         // holds chunk rows when it is below ngroups (rows past the chunk in that group repeat
         // its last row); otherwise every lane moves the same 16 bytes of the last row.  Row
         // scales: wave w moves those of rows [64w, 64w+64), clamped to the chunk.
         const int ngroups = (rc + 7) >> 3;
+        // weight-panel scales of every k-block: wave w moves panel min(w, np-1)'s into row w of
+        // s_sw (rows 0 and 1 are read; every wave issues the same DMA)
+        __builtin_amdgcn_global_load_lds(
+            w_scales + ((size_t)e * Nb + nb0 + min(wave, np - 1)) * KB + min(lane, KB - 1),
+            (lds_void*)&s_sw[wave][0], 4, 0, 0);
+        // GATHER: wave w moves the sorted route ids of chunk rows [64w, 64w+64) (clamped to the
+        // chunk) into s_ids, read after the barrier below
+        if constexpr (GATHER)
+            __builtin_amdgcn_global_load_lds(sorted_route_ids + rb + min(wave * 64 + lane, rc - 1),
+                                             (lds_void*)&s_ids[wave * 64], 4, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+
         const uint8_t* srcW[4];
         const uint8_t* srcA[4];
 #pragma unroll
@@ -167,11 +183,31 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
             const int wr = nb0 * 128 + (r < np * 128 ? r : r - 128);
             srcW[i] = w + ((size_t)e * N + wr) * K + dc * 16;
         }
-        // source row of sorted row rb + i (i < rc)
+        auto issue_w = [&](auto bt, int kb) __attribute__((always_inline)) {
+            TileStage<BM>& T = stage(bt);
+            const int k0 = kb * 128;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds(srcW[i] + k0,
+                                                 (lds_void*)&T.w[(wave * 32 + i * 8) * 8], 16,
+                                                 0, 0);
+        };
+        issue_w(std::integral_constant<int, 0>{}, 0);
+        if (S == 3 && KB > 1) issue_w(std::integral_constant<int, 1>{}, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // source row of chunk row i (i < rc)
         auto src_row = [&](int i) __attribute__((always_inline)) -> size_t {
-            if (GATHER) return (size_t)(sorted_route_ids[rb + i] / kr);
+            if (GATHER) return (size_t)(s_ids[i] / kr);
             return (size_t)(rb + i);
         };
+        if constexpr (GATHER) {
+            // every wave's ids have landed (only the weight DMAs may still be in flight)
+            if (S == 3 && KB > 1)
+                barrier_keep_vm<8>();
+            else
+                barrier_keep_vm<4>();
+        }
+
 #pragma unroll
         for (int i = 0; i < Cfg::kADma; ++i) {
             const int r = (wave + 8 * i) * 8 + dl;
@@ -181,14 +217,10 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
         const uint8_t* srcPad = a + src_row(rc - 1) * K;
         const float* srcS = a_scales + src_row(min(wave * 64 + lane, rc - 1));
 
-        auto issue = [&](auto bt, int kb) __attribute__((always_inline)) {
+        // the row DMAs (and row scales) of k-block kb into stage bt
+        auto issue_a = [&](auto bt, int kb) __attribute__((always_inline)) {
             TileStage<BM>& T = stage(bt);
             const int k0 = kb * 128;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds(srcW[i] + k0,
-                                                 (lds_void*)&T.w[(wave * 32 + i * 8) * 8], 16,
-                                                 0, 0);
 #pragma unroll
             for (int i = 0; i < Cfg::kADma; ++i) {
                 lds_void* dst = (lds_void*)&T.a[(wave + 8 * i) * 64];
@@ -199,6 +231,12 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
             __builtin_amdgcn_global_load_lds(srcS + (size_t)kb * rows,
                                              (lds_void*)&T.sa[wave * 64], 4, 0, 0);
         };
+        auto issue = [&](auto bt, int kb) __attribute__((always_inline)) {
+            issue_w(bt, kb);
+            issue_a(bt, kb);
+        };
+        issue_a(std::integral_constant<int, 0>{}, 0);
+        if (S == 3 && KB > 1) issue_a(std::integral_constant<int, 1>{}, 1);
 
         v4f acc[2][Cfg::kGroups];
 #pragma unroll
@@ -256,11 +294,18 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
             constexpr int Bi = decltype(bt)::value;
             if constexpr (S == 3) {
                 // this wave's DMA of stage kb has landed (stage kb+1's may still be in flight);
-                // the barrier publishes every wave's and frees the stage read one k-block ago
-                if (kb + 1 < KB)
-                    barrier_keep_vm<Cfg::kDma>();
-                else
+                // the barrier publishes every wave's and frees the stage read one k-block ago.
+                // The first two stages went out weights first (W0 W1 A0 S0 A1 S1, after the
+                // panel scales), so at kb = 0 only stage 1's row and scale DMAs may stay in
+                // flight.
+                if (kb + 1 < KB) {
+                    if (kb == 0)
+                        barrier_keep_vm<Cfg::kADma + 1>();
+                    else
+                        barrier_keep_vm<Cfg::kDma>();
+                } else {
                     barrier_keep_vm<0>();
+                }
                 if (kb + 2 < KB) issue(std::integral_constant<int, (Bi + 2) % 3>{}, kb + 2);
             } else {
                 // two stages: stage kb has landed everywhere and the other one is no longer read
@@ -270,8 +315,6 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
             compute(bt, kb);
         };
 
-        issue(std::integral_constant<int, 0>{}, 0);
-        if (S == 3 && KB > 1) issue(std::integral_constant<int, 1>{}, 1);
 #pragma unroll
         for (int kb = 0; kb < KB; kb += S) {
             step(std::integral_constant<int, 0>{}, kb);
