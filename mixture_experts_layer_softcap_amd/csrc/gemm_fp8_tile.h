@@ -332,8 +332,8 @@ void gemm_fp8_tile_kernel(const uint8_t* __restrict__ a, const float* __restrict
                 const int m = r * 16 + j;
                 if (r >= nrg || m >= rc) continue;
                 size_t row = (size_t)(rb + m);
-                if (EPI == MOE_EPI_ROUTE_F32 || EPI == kEpiAtomicAdd)
-                    row = (size_t)sorted_route_ids[rb + m];
+                if (EPI == MOE_EPI_ROUTE_F32 || EPI == kEpiAtomicAdd)   // (GATHER: from LDS)
+                    row = (size_t)(GATHER ? s_ids[m] : sorted_route_ids[rb + m]);
                 float wv = 0.0f;
                 if constexpr (EPI == kEpiAtomicAdd) wv = topk_weights[row];
 #pragma unroll
