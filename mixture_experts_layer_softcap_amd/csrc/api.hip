@@ -210,7 +210,7 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
         // two kernels: the route runs inside the GEMM, handing the routes over through tagged
         // words in the otherwise unused route_slots part; the combine clears them again
         uint32_t* handoff = reinterpret_cast<uint32_t*>(slots);
-        if ((e = launch_gemm_fp8_fused_route(a.logits, a.x, a.M, a.k, a.E, a.softcap, a.w_q,
+        if ((e = launch_gemm_fp8_fused_route(a.logits, a.x, a.M, a.k, a.E, a.K, a.softcap, a.w_q,
                                              a.w_scales, a.N, ids, wts, handoff,
                                              queue + MOE_QUEUE_HANDOFF_STATUS, rows,
                                              (a.flags & MOE_FWD_ROUTE_SELF) != 0, s)) !=
@@ -223,7 +223,7 @@ hipError_t enqueue_forward(const FwdArgs& a, hipStream_t s) {
     if (!(a.flags & MOE_FWD_STAGED) && forward_fused_applies(a.M, a.k, a.E, a.K, a.N, a.chunk)) {
         // small batch: layout, sort/gather and quantisation run inside the GEMM, whose fp32
         // rows land at their route ids
-        if ((e = launch_gemm_fp8_fused(a.x, ids, a.M, a.k, a.E, a.w_q, a.w_scales, a.N, rows,
+        if ((e = launch_gemm_fp8_fused(a.x, ids, a.M, a.k, a.E, a.K, a.w_q, a.w_scales, a.N, rows,
                                        s)) != hipSuccess)
             return e;
         return launch_scatter(rows, nullptr, wts, ids, a.M, a.k, a.E, a.N, a.out, s);
@@ -578,7 +578,7 @@ int moe_grouped_gemm_routed(const uint16_t* x, const int32_t* topk_ids, int M, i
     if (rc) return rc;
     if (!forward_fused_applies(M, k, E, K, N, 16)) return MOE_E_INVAL;
     const hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_gemm_fp8_fused(x, topk_ids, M, k, E, w_q, w_scales, N, rows, s);
+    hipError_t e = launch_gemm_fp8_fused(x, topk_ids, M, k, E, K, w_q, w_scales, N, rows, s);
     if (e == hipSuccess && counts) e = launch_counts(topk_ids, M, k, E, counts, offsets, s);
     return hip_status(e);
 }
@@ -596,7 +596,7 @@ int moe_route_grouped_gemm(const float* logits, const uint16_t* x, int M, int E,
     if (rc) return rc;
     if (!forward_fused_applies(M, k, E, K, N, 16) || !fused_route_applies(M, k, E))
         return MOE_E_INVAL;
-    return hip_status(launch_gemm_fp8_fused_route(logits, x, M, k, E, softcap, w_q, w_scales,
+    return hip_status(launch_gemm_fp8_fused_route(logits, x, M, k, E, K, softcap, w_q, w_scales,
                                                   N, topk_ids, topk_weights, route_words,
                                                   status, rows, false, (hipStream_t)stream));
 }
@@ -865,11 +865,11 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
         uint32_t* handoff = nullptr;
         if (fused_route_applies(M, k, E)) {
             handoff = reinterpret_cast<uint32_t*>(slots);
-            e = launch_gemm_fp8_fused_route(logits, x, M, k, E, softcap, w1_q, w1_scales, 2 * I,
+            e = launch_gemm_fp8_fused_route(logits, x, M, k, E, H, softcap, w1_q, w1_scales, 2 * I,
                                             ids, wts, handoff, queue + MOE_QUEUE_HANDOFF_STATUS,
                                             h1, false, s);
         } else if ((e = launch_route(logits, M, E, k, softcap, ids, wts, s)) == hipSuccess) {
-            e = launch_gemm_fp8_fused(x, ids, M, k, E, w1_q, w1_scales, 2 * I, h1, s);
+            e = launch_gemm_fp8_fused(x, ids, M, k, E, H, w1_q, w1_scales, 2 * I, h1, s);
         }
         if (e != hipSuccess ||
             (e = launch_layout_swiglu(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td,

@@ -59,19 +59,16 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRing = 16;                     // k-block units per wave in registers
-constexpr int kK = 2048;
-constexpr int kKB = kK / 128;                 // k-blocks per row
-constexpr int kPasses = kKB / kRing;
 constexpr int kMaxRoutes = 2048;              // M * k
 constexpr int kMaxLocal = 4;                  // experts touched by one workgroup's range
 constexpr int kTiles = 4;                     // resident 16-row tiles
-constexpr int kXSteps = 256 / 4 / kWaves;     // x loads per lane for one tile
 constexpr int kRouteVPL = 4;                  // ROUTE form: logits per lane, E <= 256
 
+// KB = K / 128 k-blocks per row: 2, 4, 8 or 16 (K = 256 .. 2048)
+template <int KB>
 struct FusedLds {
-    uint4 frag[kTiles][kKB * 2 * 64];         // fragment f = (k-block f/2, half f%2)
-    float sa[kTiles][kKB * 16];               // [k-block][row]
+    uint4 frag[kTiles][KB * 2 * 64];          // fragment f = (k-block f/2, half f%2)
+    float sa[kTiles][KB * 16];                // [k-block][row]
     int list[kMaxRoutes];                     // (token << 12) | route, expert-major
     int cnt[kMaxLocal];                       // routes per local expert
     int first[kMaxLocal];                     // list position of its first route
@@ -118,12 +115,17 @@ __device__ __forceinline__ int scan512_small(int c, int* s_w, int& total) {
     return base + below;
 }
 
-template <bool NT, bool ROUTE>
+template <int KB, bool NT, bool ROUTE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, int R, int k,
                            const uint8_t* w, const float* __restrict__ w_scales, int N,
                            int slices, float* __restrict__ rows_out, FusedRoute rt) {
-    __shared__ FusedLds L;
+    constexpr int kKB = KB;                     // k-blocks per row
+    constexpr int kK = KB * 128;
+    constexpr int kRing = KB < 16 ? KB : 16;    // k-block units per wave in registers
+    constexpr int kPasses = kKB / kRing;
+    constexpr int kXSteps = KB / 2;             // x loads per lane for one tile (16 * KB blocks)
+    __shared__ FusedLds<KB> L;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,7 +183,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
     // ids goes a small first burst: the first kPre units of the wave's first slice of the
     // range (unless routing moves the wave's start, the slice it will stream first).  It keeps
     // the memory busy while the tiles are built, yet drains before the x rows are requested.
-    constexpr int kPre = ROUTE ? 6 : 4;
+    constexpr int kPre = (ROUTE ? 6 : 4) < kRing ? (ROUTE ? 6 : 4) : kRing;
     const int s_pre = min(lo + wave, hi - 1);
     int v[4];
     if constexpr (!ROUTE) {
@@ -325,7 +327,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
                 L.trc[t] = rc;
                 L.tlb[t] = lb;
             }
-            // step st covers blocks 4*st .. 4*st+3 (row b>>4, k-block b&15), one per 16 lanes;
+            // step st covers blocks 4*st .. 4*st+3 (row b/KB, k-block b%KB), one per 16 lanes;
             // rows past rc are not quantised (their columns are not stored); their lanes still
             // load, unconditionally, but all from the first 256 bytes of x, which stay in the
             // CU's L1 and take no place among its requests to L2 (at a few routes per expert
@@ -334,7 +336,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
 #pragma unroll
             for (int i8 = 0; i8 < kXSteps; ++i8) {
                 const int bq = (wave + i8 * kWaves) * 4 + g;
-                const int jj = bq >> 4, kb = bq & 15;
+                const int jj = bq / kKB, kb = bq % kKB;
                 const int ent = L.list[lb + (jj < rc ? jj : 0)];
                 const size_t off = jj < rc ? (size_t)(ent >> 12) * kK + kb * 128 : 0;
                 xr[i8] = *reinterpret_cast<const uint4*>(x + off + j * 8);
@@ -356,7 +358,7 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
 #pragma unroll
             for (int i8 = 0; i8 < kXSteps; ++i8) {
                 const int bq = (wave + i8 * kWaves) * 4 + g;
-                const int jj = bq >> 4, kb = bq & 15;
+                const int jj = bq / kKB, kb = bq % kKB;
                 if (jj < rc) {                  // whole 16-lane groups
                     const Quant8 qv = quantise8(xr[i8], true);
                     const int el = j * 8;       // element offset inside the 128-value block
@@ -482,7 +484,7 @@ int fused_max_local_experts(int E, int N, int grid) {
 }
 
 bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows) {
-    return K == kK && chunk_rows == 16 && (long long)M * k <= kMaxRoutes && N % 128 == 0 &&
+    return (K == 256 || K == 512 || K == 1024 || K == 2048) && chunk_rows == 16 && (long long)M * k <= kMaxRoutes && N % 128 == 0 &&
            fused_max_local_experts(E, N, device_info().cu_count) <= kMaxLocal;
 }
 
@@ -491,19 +493,40 @@ bool fused_route_applies(int M, int k, int E) {
            k <= 64;
 }
 
-hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
-                                 const uint8_t* w, const float* w_scales, int N,
-                                 float* rows_out, hipStream_t s) {
+namespace {
+
+// one launch of the kernel for K = 128 * KB
+template <bool ROUTE>
+hipError_t launch_fused_k(int K, const uint16_t* x, const int32_t* ids, int R, int k,
+                          const uint8_t* w, const float* w_scales, int N, int slices,
+                          float* rows_out, const FusedRoute& rt, hipStream_t s) {
     const int grid = device_info().cu_count;    // one 8-wave workgroup per CU
-    const int slices = E * (N / 16);
-    const FusedRoute none{};
-    hipLaunchKernelGGL((gemm_fp8_fused_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s,
-                       x, ids, M * k, k, w, w_scales, N, slices, rows_out, none);
+#define MOE_FUSED_LAUNCH(KB_)                                                                     \
+    hipLaunchKernelGGL((gemm_fp8_fused_kernel<KB_, true, ROUTE>), dim3(grid), dim3(kThreads), 0, \
+                       s, x, ids, R, k, w, w_scales, N, slices, rows_out, rt)
+    switch (K) {
+        case 256: MOE_FUSED_LAUNCH(2); break;
+        case 512: MOE_FUSED_LAUNCH(4); break;
+        case 1024: MOE_FUSED_LAUNCH(8); break;
+        case 2048: MOE_FUSED_LAUNCH(16); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MOE_FUSED_LAUNCH
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
+                                 int K, const uint8_t* w, const float* w_scales, int N,
+                                 float* rows_out, hipStream_t s) {
+    const FusedRoute none{};
+    return launch_fused_k<false>(K, x, ids, M * k, k, w, w_scales, N, E * (N / 16), rows_out,
+                                 none, s);
+}
+
 hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, int M, int k,
-                                       int E, float softcap, const uint8_t* w,
+                                       int E, int K, float softcap, const uint8_t* w,
                                        const float* w_scales, int N, int32_t* ids,
                                        float* weights, uint32_t* handoff, uint32_t* status,
                                        float* rows_out, bool self_route, hipStream_t s) {
@@ -512,12 +535,10 @@ hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, i
     // a routing wave normally publishes within a few microseconds; 4096 rounds of polls
     // (milliseconds) only run out when its workgroup waits for a CU another kernel holds
     const int max_polls = self_route ? 0 : 4096;
-    const int grid = device_info().cu_count;    // every token's routing wave is in the grid
-    const int slices = E * (N / 16);
+    // (one workgroup per CU: every token's routing wave is in the grid)
     const FusedRoute rt{logits, ids, weights, handoff, status, tag, max_polls, M, E, softcap};
-    hipLaunchKernelGGL((gemm_fp8_fused_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s,
-                       x, nullptr, M * k, k, w, w_scales, N, slices, rows_out, rt);
-    return hipGetLastError();
+    return launch_fused_k<true>(K, x, nullptr, M * k, k, w, w_scales, N, E * (N / 16), rows_out,
+                                rt, s);
 }
 
 }  // namespace moe

@@ -119,7 +119,7 @@ hipError_t launch_acc_to_bf16(const float* acc, int M, int N, uint16_t* out, hip
 // slices split evenly over one workgroup per CU, fp32 rows at route ids ([M*k][N])
 bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows);
 hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
-                                 const uint8_t* w, const float* w_scales, int N,
+                                 int K, const uint8_t* w, const float* w_scales, int N,
                                  float* rows_out, hipStream_t s);
 // The same GEMM with the route inside (moe_route folded in): writes ids and weights, hands
 // the routes over through tagged words handoff [M*k] (untagged at launch; cleared by the
@@ -127,7 +127,7 @@ hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, i
 // fused_route_applies also holds.
 bool fused_route_applies(int M, int k, int E);
 hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, int M, int k,
-                                       int E, float softcap, const uint8_t* w,
+                                       int E, int K, float softcap, const uint8_t* w,
                                        const float* w_scales, int N, int32_t* ids,
                                        float* weights, uint32_t* handoff, uint32_t* status,
                                        float* rows_out, bool self_route, hipStream_t s);

@@ -149,6 +149,8 @@ def ws_part(ws, d, which, dtype, n):
                                       # route inside, layout and activations in one launch,
                                       # down GEMM gathering its rows by sorted route id
     (64, 8, 2, 2048, 512, 128, 7),    # LDS-tiled GEMM for both projections
+    (64, 8, 2, 1024, 512, 16, 4),     # small batch at hidden width 1024
+    (40, 16, 3, 512, 1024, 0, 4),     # ... and 512, expert width 1024
 ])
 def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
     assert moe.mlp_forward_kernels(M, E, k, H, I, chunk) == kernels

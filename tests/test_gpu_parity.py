@@ -769,7 +769,7 @@ def test_forward_full(name, flags):
         np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, d["E"]), ref["counts"])
         np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, d["E"] + 1), ref["offsets"])
     else:
-        assert not flags & moe.MOE_FWD_STAGED and name == QWEN
+        assert not flags & moe.MOE_FWD_STAGED
 
 
 @pytest.mark.parametrize("chunk", [0, 64, 256])
@@ -996,6 +996,31 @@ def test_forward_fused_route_matches_three_kernels(M, E, k, N, mode):
     assert_bf16_close(base[0], ref["y64"], f"fused route M={M} E={E} k={k} N={N}")
 
 
+@pytest.mark.parametrize("K", [256, 512, 1024])
+@pytest.mark.parametrize("M,E,k,N", [
+    (8, 16, 2, 256),        # the tiny layer
+    (120, 64, 8, 128),      # 960 routes, 15 per expert
+    (33, 40, 5, 384),       # E not a multiple of 64, three panels
+])
+def test_forward_small_batch_depths(M, E, k, N, K):
+    # the small-batch GEMM at the depths below 2048: the route inside (two kernels) and as a
+    # kernel of its own (three) give the same bits, and both match the oracle; the staged
+    # step (five kernels) matches it too
+    d = synth.fused_inputs(M, E, k, K, N, seed=M + E + K)
+    d.update(M=M, E=E, k=k, K=K, N=N)
+    d["w_q"], d["w_s"] = orc.quant_weights(d["w"])
+    ref = orc.forward(d["logits"], d["x"], d["w_q"], d["w_s"], k, CAP)
+    assert moe.forward_kernels(M, E, k, K, N, 0, 0) == 2
+    assert moe.forward_kernels(M, E, k, K, N, 0, moe.MOE_FWD_ROUTE_KERNEL) == 3
+    two = gpu_forward(d, reps=2)
+    three = gpu_forward(d, flags=moe.MOE_FWD_ROUTE_KERNEL)[0]
+    staged = gpu_forward(d, flags=moe.MOE_FWD_STAGED)[0]
+    for y in two:
+        np.testing.assert_array_equal(y, three)
+    assert_bf16_close(three, ref["y64"], f"small batch M={M} E={E} k={k} K={K} N={N}")
+    assert_bf16_close(staged, ref["y64"], f"staged M={M} E={E} k={k} K={K} N={N}")
+
+
 @pytest.mark.parametrize("flags", [0, 256])
 def test_forward_fused_route_ties_and_non_finite_logits(flags):
     # the route inside the GEMM (handed over, or taken by every wave itself: flags 256 =
@@ -1025,13 +1050,16 @@ def test_forward_fused_route_ties_and_non_finite_logits(flags):
 
 
 def test_forward_fused_route_only_where_it_applies():
-    # the route moves into the GEMM by default on the small-batch path with E <= 256; E above
-    # 256, a batch outside that path, the staged flag or MOE_FWD_ROUTE_KERNEL keep the route
-    # kernel
+    # the route moves into the GEMM by default on the small-batch path (K = 256, 512, 1024 or
+    # 2048) with E <= 256; E above 256, a batch outside that path, another K, the staged flag
+    # or MOE_FWD_ROUTE_KERNEL keep the route kernel
     assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, 0) == 2
     assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, moe.MOE_FWD_ROUTE_KERNEL) == 3
     assert moe.forward_kernels(100, 300, 3, 2048, 384, 0, 0) == 3
-    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, 0) == 5
+    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, 0) == 2
+    assert moe.forward_kernels(8, 16, 2, 256, 256, 0, moe.MOE_FWD_ROUTE_KERNEL) == 3
+    assert moe.forward_kernels(8, 16, 2, 384, 256, 0, 0) == 5
+    assert moe.forward_kernels(8, 16, 2, 4096, 256, 0, 0) == 5
     assert moe.forward_kernels(1024, 256, 8, 2048, 512, 0, 0) == 4
     assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, moe.MOE_FWD_STAGED) == 5
 
