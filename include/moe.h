@@ -263,7 +263,8 @@ int moe_grouped_gemm_gather(const uint8_t* x_q, const float* x_scales, int M, in
                             uint32_t* queue, int sched, moe_stream_t stream);
 
 /* ---- [FMF8] Baseline items 2-6 fused: grouped FP8 GEMM straight from routed ids ------------
- * The small-batch GEMM of moe_forward: K = 2048, M*k <= 2048, N a multiple of 128, and E at
+ * The small-batch GEMM of moe_forward: K = 256, 512, 1024 or 2048, M*k <= 2048, N a multiple
+ * of 128, and E at
  * most about three times the CU count (one CU's share of the E*N/16 weight slices may touch at
  * most four experts).  The weights are split evenly over one workgroup per CU, independent of
  * the routing; each workgroup finds its experts' routes in topk_ids [M][k] (ascending route
@@ -427,7 +428,8 @@ int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_sca
  * [M*k][2I], 13 act codes [M*k][I], 14 act scales [I/128][M*k], 15 down rows f32 [M*k][H]
  * at route ids.  Seven plain launches on `stream` (one layout pass writes both task lists),
  * no host synchronisation.  Small batches (the small-batch FP8 GEMM of moe_grouped_gemm_routed
- * applies to the gate+up projection, chunk_rows 16, I in {512, 1024, 2048}) take four: the
+ * applies to the gate+up projection: H in {256, 512, 1024, 2048}, chunk_rows 16, and
+ * I in {512, 1024, 2048}) take four: the
  * gate+up GEMM from the routed ids with the route inside it (as moe_route_grouped_gemm; route
  * words in part 9, its status word at word MOE_QUEUE_HANDOFF_STATUS of the first task
  * counters in part 7; a separate route kernel first where E > 256 or M is above 8 per CU:

@@ -1,7 +1,8 @@
 // fused_fp8.hip -- small-batch grouped FP8 GEMM straight from the routed ids: the layout,
 // sort/gather and quantisation stages ([FMF8] "Baseline: 7 kernels" items 2-5, Fusion 2 and 3)
 // folded into the grouped GEMM (item 6, per-K-block scaling) for at most 2048 routed rows and
-// K = 2048 -- the decode-sized regime of the pages' problem table (a few rows per expert).
+// K = 256, 512, 1024 or 2048 -- the decode-sized regime of the pages' problem table (a few rows
+// per expert).
 //
 // Work split.  The weights, not the routed rows, are divided among the workgroups: the E*N/16
 // slices of 16 weight rows x K bytes, in expert-major order, are cut into one contiguous range
@@ -17,7 +18,7 @@
 // more routed rows than fit goes round by round, its slices streamed once per round.
 //
 // Weights.  Each wave walks every 8th slice of the round (and, for an expert with several
-// resident tiles, each slice once per tile) with a ring of kRing = 16 k-block units in
+// resident tiles, each slice once per tile) with a ring of kRing = K/128 k-block units in
 // registers -- a whole slice, two 16-byte loads per lane per unit -- refilling each unit right
 // after its MFMA with the same k-block of the wave's next item, so the stream does not pause
 // between items.
