@@ -482,10 +482,10 @@ def bench_mlp(args, moe, synth, torch, np):
     lbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4) \
         + M * E * 4 + M * H * 2 + M * H * 2
     flops = 2.0 * R * (N1 * H + H * I)
-    gemm_kernel = ("gemm_fp8_fused_kernel<true, true> (the route inside the gate+up grouped "
-                   "FP8 GEMM from routed ids, rows at route ids)" if nkern == 4 else
-                   "gemm_fp8_fused_kernel<true, false> (gate+up grouped FP8 GEMM from routed "
-                   "ids, rows at route ids)" if fused else
+    gemm_kernel = (f"gemm_fp8_fused_kernel<{H // 128}, true, true> (the route inside the "
+                   "gate+up grouped FP8 GEMM from routed ids, rows at route ids)" if nkern == 4 else
+                   f"gemm_fp8_fused_kernel<{H // 128}, true, false> (gate+up grouped FP8 GEMM "
+                   "from routed ids, rows at route ids)" if fused else
                    "gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
                    if H == 2048 and chunk <= 16 else
                    "gemm_fp8_tile_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
@@ -724,11 +724,11 @@ def main():
         gemm_kernel = ("gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles gathered from "
                        "token-major rows, ROUTE_F32)")
     elif nkern == 2:
-        gemm_kernel = ("gemm_fp8_fused_kernel<true, true> (the route inside the grouped FP8 GEMM "
-                       "from routed ids, rows at route ids)")
+        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, true> (the route inside the "
+                       "grouped FP8 GEMM from routed ids, rows at route ids)")
     elif fused:
-        gemm_kernel = ("gemm_fp8_fused_kernel<true, false> (grouped FP8 GEMM from routed ids, "
-                       "rows at route ids)")
+        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, false> (grouped FP8 GEMM from "
+                       "routed ids, rows at route ids)")
     elif K in (512, 1024, 2048) and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
     elif 64 < chunk <= 256 and K <= 8192:
