@@ -423,9 +423,9 @@ def bench_mlp(args, moe, synth, torch, np):
     R = M * k
     chunk = args.chunk_rows or (16 if -(-R // E) <= 16 else (128 if H <= 8192 else 64))
     nkern = moe.mlp_forward_kernels(M, E, k, H, I, args.chunk_rows)
-    fused = nkern in (4, 5)
+    fused = nkern in (3, 4)
     h1 = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
-    if nkern == 4:
+    if nkern == 3:
         # the gate+up GEMM alone with the route inside, as the step runs it
         ids_b = torch.empty((M, k), dtype=torch.int32, device=dev)
         wts_b = torch.empty((M, k), dtype=torch.float32, device=dev)
@@ -475,7 +475,7 @@ def bench_mlp(args, moe, synth, torch, np):
     counts = np.bincount(ids_np, minlength=E)
     nonempty = int((counts > 0).sum())
     N1 = 2 * I
-    acts = (M * H * 2 + M * E * 4 + R * 8) if nkern == 4 else \
+    acts = (M * H * 2 + M * E * 4 + R * 8) if nkern == 3 else \
         (M * H * 2 + R * 4) if fused else (R * H + (H // 128) * R * 4 + R * 4)
     gbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4) + acts + R * N1 * 4
     achieved = gbytes / (gemm_us * 1e-6) / 1e9
@@ -483,7 +483,7 @@ def bench_mlp(args, moe, synth, torch, np):
         + M * E * 4 + M * H * 2 + M * H * 2
     flops = 2.0 * R * (N1 * H + H * I)
     gemm_kernel = (f"gemm_fp8_fused_kernel<{H // 128}, true, true> (the route inside the "
-                   "gate+up grouped FP8 GEMM from routed ids, rows at route ids)" if nkern == 4 else
+                   "gate+up grouped FP8 GEMM from routed ids, rows at route ids)" if nkern == 3 else
                    f"gemm_fp8_fused_kernel<{H // 128}, true, false> (gate+up grouped FP8 GEMM "
                    "from routed ids, rows at route ids)" if fused else
                    "gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
@@ -499,12 +499,12 @@ def bench_mlp(args, moe, synth, torch, np):
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "E": E, "top_k": k, "H": H, "I": I,
                    "softcap": cap, "weight_copies_rotated": copies, "chunk_rows": chunk,
-                   "path": ("4 kernels: gate+up GEMM routing its tokens itself, layout (down "
-                            "tasks, sorted ids) with silu*up requantise in one launch, down GEMM "
-                            "gathering by sorted id, combine" if nkern == 4 else
-                            "5 kernels: route, gate+up GEMM from the routed ids, layout (down "
-                            "tasks, sorted ids) with silu*up requantise in one launch, down GEMM "
-                            "gathering by sorted id, combine" if fused else
+                   "path": ("3 kernels: gate+up GEMM routing its tokens itself, down GEMM "
+                            "from the same ids forming silu*up and requantising it in its tile "
+                            "build, combine" if nkern == 3 else
+                            "4 kernels: route, gate+up GEMM from the routed ids, down GEMM from "
+                            "the same ids forming silu*up and requantising it in its tile build, "
+                            "combine" if fused else
                             "7 kernels: route, layout (both task lists), QSG, gate+up GEMM, "
                             "silu*up requantise, down GEMM, combine")},
         "effective_tflops": round(flops / (us * 1e-6) / 1e12, 3),

@@ -428,16 +428,17 @@ int moe_swiglu_quant(const float* h, int rows, int I, uint8_t* a_q, float* a_sca
  * [M*k][2I], 13 act codes [M*k][I], 14 act scales [I/128][M*k], 15 down rows f32 [M*k][H]
  * at route ids.  Seven plain launches on `stream` (one layout pass writes both task lists),
  * no host synchronisation.  Small batches (the small-batch FP8 GEMM of moe_grouped_gemm_routed
- * applies to the gate+up projection: H in {256, 512, 1024, 2048}, chunk_rows 16, and
- * I in {512, 1024, 2048}) take four: the
- * gate+up GEMM from the routed ids with the route inside it (as moe_route_grouped_gemm; route
- * words in part 9, its status word at word MOE_QUEUE_HANDOFF_STATUS of the first task
+ * applies to both projections: H and I in {256, 512, 1024, 2048}, chunk_rows 16) take three:
+ * the gate+up GEMM from the routed ids with the route inside it (as moe_route_grouped_gemm;
+ * route words in part 9, its status word at word MOE_QUEUE_HANDOFF_STATUS of the first task
  * counters in part 7; a separate route kernel first where E > 256 or M is above 8 per CU:
- * five) with rows at route ids in part 12 (parts 10-11 unused) -> one launch holding both the
- * layout of the down projection with sorted route ids and moe_swiglu_quant in route order ->
- * down GEMM gathering its rows by sorted route id -> combine. */
+ * four) with rows at route ids in part 12 -> the down GEMM from the same ids, forming
+ * silu(g) * u of each of its rows from part 12 and requantising it per 128 columns in its
+ * tile build as moe_swiglu_quant would (those codes and scales also land in parts 13-14, in
+ * route order) -> combine.  That path writes no counts, offsets, tasks or sorted ids (parts
+ * 2-8 and 10-11 unused). */
 size_t moe_mlp_workspace_bytes(int M, int E, int k, int H, int I);
-/* Number of kernels moe_mlp_forward launches for these arguments (4, 5 or 7); MOE_E_INVAL for
+/* Number of kernels moe_mlp_forward launches for these arguments (3, 4 or 7); MOE_E_INVAL for
  * arguments it rejects, MOE_E_DEVICE without a gfx950 device. */
 int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows);
 int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which);

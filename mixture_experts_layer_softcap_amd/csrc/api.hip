@@ -799,6 +799,19 @@ int64_t moe_mlp_workspace_offset(int M, int E, int k, int H, int I, int which) {
     return (int64_t)mlp_layout(M, E, k, H, I).off[which];
 }
 
+}  // extern "C"
+
+namespace {
+// Both projections of the FP8 MLP fit the small-batch GEMM: gate+up [M*k] x [2I, H] and down
+// [M*k] x [H, I] with its activation step in the tile build.
+bool mlp_small_batch(int M, int k, int E, int H, int I, int chunk) {
+    return forward_fused_applies(M, k, E, H, 2 * I, chunk) &&
+           forward_fused_applies(M, k, E, I, H, chunk);
+}
+}  // namespace
+
+extern "C" {
+
 int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows) {
     if (!mlp_dims_ok(M, E, k, H, I)) return MOE_E_INVAL;
     const int Kmax = H > I ? H : I;
@@ -808,9 +821,8 @@ int moe_mlp_forward_kernels(int M, int E, int k, int H, int I, int chunk_rows) {
     if (rc) return rc;
     int chunk = chunk_rows ? chunk_rows : default_chunk(M, k, E, H);
     if (!chunk_rows && chunk > 64 && Kmax > 8192) chunk = 64;
-    if (!forward_fused_applies(M, k, E, H, 2 * I, chunk) || !gemm_fp8_range_applies(I, chunk))
-        return 7;
-    return fused_route_applies(M, k, E) ? 4 : 5;
+    if (!mlp_small_batch(M, k, E, H, I, chunk)) return 7;
+    return fused_route_applies(M, k, E) ? 3 : 4;
 }
 
 int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
@@ -856,12 +868,13 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
     const int mtd = (int)max_tasks_ll(M, k, E, nbd, chunk);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (forward_fused_applies(M, k, E, H, 2 * I, chunk) && gemm_fp8_range_applies(I, chunk)) {
+    if (mlp_small_batch(M, k, E, H, I, chunk)) {
         // small batch: the gate+up GEMM straight from the routed ids (layout, gather and
         // quantisation of x inside; the route too where it can, handing the routes over
         // through tagged words in the unused route_slots part) with rows at route ids; the
-        // down projection's layout shares a launch with the activation step; the activations
-        // stay in route order and the down GEMM gathers its rows by sorted route id
+        // down GEMM the same way from the same ids, forming and requantising the activations
+        // of its rows in its tile build (their codes and scales also land in parts 13-14, in
+        // route order)
         uint32_t* handoff = nullptr;
         if (fused_route_applies(M, k, E)) {
             handoff = reinterpret_cast<uint32_t*>(slots);
@@ -872,12 +885,8 @@ int moe_mlp_forward(const float* logits, const uint16_t* x, const uint8_t* w1_q,
             e = launch_gemm_fp8_fused(x, ids, M, k, E, H, w1_q, w1_scales, 2 * I, h1, s);
         }
         if (e != hipSuccess ||
-            (e = launch_layout_swiglu(ids, M, k, E, nbd, chunk, counts, offsets, cursors, td,
-                                      nt + 1, queue2, sorted, h1, I, aq, as, s)) !=
-                hipSuccess ||
-            (e = launch_gemm_fp8_range(aq, as, R, I, w2_q, w2_scales, H, td, nt + 1, mtd,
-                                       MOE_EPI_ROUTE_F32, sorted, h2, s, sorted)) !=
-                hipSuccess ||
+            (e = launch_gemm_fp8_fused_act(h1, ids, M, k, E, I, w2_q, w2_scales, H, h2, aq, as,
+                                           s)) != hipSuccess ||
             (e = launch_scatter(h2, nullptr, wts, ids, M, k, E, H, out, s, handoff,
                                 handoff ? R : 0)) != hipSuccess)
             return hip_status(e);

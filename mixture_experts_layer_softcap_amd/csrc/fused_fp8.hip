@@ -92,6 +92,14 @@ struct FusedRoute {
     float softcap;
 };
 
+// ACT form (the FP8 MLP's down projection): the A rows are act = silu(g) * u of the fp32
+// gate+up rows h [R][2K] at route ids, requantised per 128 columns as by moe_swiglu_quant;
+// the codes [R][K] and scales [K/128][R] also go to a_q / a_s when those are set.
+struct FusedAct {
+    uint8_t* a_q;
+    float* a_s;
+};
+
 // Workgroup barrier for LDS data only: vector-memory operations stay in flight.
 __device__ __forceinline__ void barrier_lds() { barrier_keep_vm<63>(); }
 
@@ -116,11 +124,15 @@ __device__ __forceinline__ int scan512_small(int c, int* s_w, int& total) {
     return base + below;
 }
 
-template <int KB, bool NT, bool ROUTE>
+template <int KB, bool NT, bool ROUTE, bool ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, int R, int k,
+void gemm_fp8_fused_kernel(const void* xin, const int32_t* __restrict__ ids, int R, int k,
                            const uint8_t* w, const float* __restrict__ w_scales, int N,
-                           int slices, float* __restrict__ rows_out, FusedRoute rt) {
+                           int slices, float* __restrict__ rows_out, FusedRoute rt,
+                           FusedAct act) {
+    static_assert(!(ROUTE && ACT), "the ACT form reads routed ids");
+    const uint16_t* x = static_cast<const uint16_t*>(xin);      // bf16 [M][K]
+    const float* hin = static_cast<const float*>(xin);          // ACT: fp32 [R][2K]
     constexpr int kKB = KB;                     // k-blocks per row
     constexpr int kK = KB * 128;
     constexpr int kRing = KB < 16 ? KB : 16;    // k-block units per wave in registers
@@ -334,13 +346,26 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
             // CU's L1 and take no place among its requests to L2 (at a few routes per expert
             // most of a tile is padding)
             uint4 xr[kXSteps];
+            float4 hg0[ACT ? kXSteps : 1], hg1[ACT ? kXSteps : 1];
+            float4 hu0[ACT ? kXSteps : 1], hu1[ACT ? kXSteps : 1];
 #pragma unroll
             for (int i8 = 0; i8 < kXSteps; ++i8) {
                 const int bq = (wave + i8 * kWaves) * 4 + g;
                 const int jj = bq / kKB, kb = bq % kKB;
                 const int ent = L.list[lb + (jj < rc ? jj : 0)];
-                const size_t off = jj < rc ? (size_t)(ent >> 12) * kK + kb * 128 : 0;
-                xr[i8] = *reinterpret_cast<const uint4*>(x + off + j * 8);
+                if constexpr (ACT) {
+                    // gate and up values of columns kb*128 + 8j .. +8 of the route's row (rows
+                    // past rc read route 0's row)
+                    const float* hr = hin + (jj < rc ? (size_t)(ent & 0xFFF) * 2 * kK : 0) +
+                                      kb * 128 + j * 8;
+                    hg0[i8] = *reinterpret_cast<const float4*>(hr);
+                    hg1[i8] = *reinterpret_cast<const float4*>(hr + 4);
+                    hu0[i8] = *reinterpret_cast<const float4*>(hr + kK);
+                    hu1[i8] = *reinterpret_cast<const float4*>(hr + kK + 4);
+                } else {
+                    const size_t off = jj < rc ? (size_t)(ent >> 12) * kK + kb * 128 : 0;
+                    xr[i8] = *reinterpret_cast<const uint4*>(x + off + j * 8);
+                }
             }
             MOE_WAIT_VMCNT(0);
             if (BURST) {
@@ -361,7 +386,20 @@ void gemm_fp8_fused_kernel(const uint16_t* x, const int32_t* __restrict__ ids, i
                 const int bq = (wave + i8 * kWaves) * 4 + g;
                 const int jj = bq / kKB, kb = bq % kKB;
                 if (jj < rc) {                  // whole 16-lane groups
-                    const Quant8 qv = quantise8(xr[i8], true);
+                    Quant8 qv;
+                    if constexpr (ACT) {
+                        float v[8];
+                        silu_mul8(hg0[i8], hg1[i8], hu0[i8], hu1[i8], v);
+                        qv = quantise8_f32(v, true);
+                        if (act.a_q) {          // the codes in route order, as moe_swiglu_quant
+                            const int route = L.list[lb + jj] & 0xFFF;
+                            *reinterpret_cast<uint2*>(act.a_q + (size_t)route * kK + kb * 128 +
+                                                      j * 8) = qv.codes;
+                            if (j == 0) act.a_s[(size_t)kb * R + route] = qv.scale;
+                        }
+                    } else {
+                        qv = quantise8(xr[i8], true);
+                    }
                     const int el = j * 8;       // element offset inside the 128-value block
                     const int f = kb * 2 + (el >> 6);
                     uint8_t* dst = reinterpret_cast<uint8_t*>(
@@ -497,14 +535,16 @@ bool fused_route_applies(int M, int k, int E) {
 namespace {
 
 // one launch of the kernel for K = 128 * KB
-template <bool ROUTE>
-hipError_t launch_fused_k(int K, const uint16_t* x, const int32_t* ids, int R, int k,
+template <bool ROUTE, bool ACT>
+hipError_t launch_fused_k(int K, const void* x, const int32_t* ids, int R, int k,
                           const uint8_t* w, const float* w_scales, int N, int slices,
-                          float* rows_out, const FusedRoute& rt, hipStream_t s) {
+                          float* rows_out, const FusedRoute& rt, const FusedAct& act,
+                          hipStream_t s) {
     const int grid = device_info().cu_count;    // one 8-wave workgroup per CU
 #define MOE_FUSED_LAUNCH(KB_)                                                                     \
-    hipLaunchKernelGGL((gemm_fp8_fused_kernel<KB_, true, ROUTE>), dim3(grid), dim3(kThreads), 0, \
-                       s, x, ids, R, k, w, w_scales, N, slices, rows_out, rt)
+    hipLaunchKernelGGL((gemm_fp8_fused_kernel<KB_, true, ROUTE, ACT>), dim3(grid),               \
+                       dim3(kThreads), 0, s, x, ids, R, k, w, w_scales, N, slices, rows_out, rt, \
+                       act)
     switch (K) {
         case 256: MOE_FUSED_LAUNCH(2); break;
         case 512: MOE_FUSED_LAUNCH(4); break;
@@ -522,8 +562,18 @@ hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, i
                                  int K, const uint8_t* w, const float* w_scales, int N,
                                  float* rows_out, hipStream_t s) {
     const FusedRoute none{};
-    return launch_fused_k<false>(K, x, ids, M * k, k, w, w_scales, N, E * (N / 16), rows_out,
-                                 none, s);
+    const FusedAct no_act{};
+    return launch_fused_k<false, false>(K, x, ids, M * k, k, w, w_scales, N, E * (N / 16),
+                                        rows_out, none, no_act, s);
+}
+
+hipError_t launch_gemm_fp8_fused_act(const float* h, const int32_t* ids, int M, int k, int E,
+                                     int K, const uint8_t* w, const float* w_scales, int N,
+                                     float* rows_out, uint8_t* a_q, float* a_s, hipStream_t s) {
+    const FusedRoute none{};
+    const FusedAct act{a_q, a_s};
+    return launch_fused_k<false, true>(K, h, ids, M * k, k, w, w_scales, N, E * (N / 16),
+                                       rows_out, none, act, s);
 }
 
 hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, int M, int k,
@@ -538,8 +588,9 @@ hipError_t launch_gemm_fp8_fused_route(const float* logits, const uint16_t* x, i
     const int max_polls = self_route ? 0 : 4096;
     // (one workgroup per CU: every token's routing wave is in the grid)
     const FusedRoute rt{logits, ids, weights, handoff, status, tag, max_polls, M, E, softcap};
-    return launch_fused_k<true>(K, x, nullptr, M * k, k, w, w_scales, N, E * (N / 16), rows_out,
-                                rt, s);
+    const FusedAct no_act{};
+    return launch_fused_k<true, false>(K, x, nullptr, M * k, k, w, w_scales, N, E * (N / 16),
+                                       rows_out, rt, no_act, s);
 }
 
 }  // namespace moe

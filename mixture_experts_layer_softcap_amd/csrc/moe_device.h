@@ -309,6 +309,23 @@ __device__ __forceinline__ void barrier_keep_vm() {
 // [I/128][R].  Lane l holds columns [8l, 8l+8) of the piece, so a 128-column block is an
 // aligned group of 16 lanes (I is a multiple of 128: a group lies wholly inside or outside
 // the row).
+// act = silu(g) * u in fp32 for 8 columns: gate values g0, g1 and up values u0, u1
+__device__ __forceinline__ void silu_mul8(const float4& g0, const float4& g1, const float4& u0,
+                                          const float4& u1, float (&v)[8]) {
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+}
+
+// the same for columns [c, c+8) of one gate+up row hr [2I] (gate columns first; c a multiple
+// of 8 below I)
+__device__ __forceinline__ void swiglu8(const float* __restrict__ hr, int I, int c, float (&v)[8]) {
+    silu_mul8(*reinterpret_cast<const float4*>(hr + c), *reinterpret_cast<const float4*>(hr + c + 4),
+              *reinterpret_cast<const float4*>(hr + I + c),
+              *reinterpret_cast<const float4*>(hr + I + c + 4), v);
+}
+
 __device__ __forceinline__ void swiglu_quant_piece(const float* __restrict__ h, int R, int I,
                                                    uint8_t* __restrict__ a_q,
                                                    float* __restrict__ a_scales,
@@ -320,15 +337,7 @@ __device__ __forceinline__ void swiglu_quant_piece(const float* __restrict__ h, 
     const bool valid = c < I;
     float v[8];
     if (valid) {
-        const float* hr = h + (size_t)r * 2 * I;
-        const float4 g0 = *reinterpret_cast<const float4*>(hr + c);
-        const float4 g1 = *reinterpret_cast<const float4*>(hr + c + 4);
-        const float4 u0 = *reinterpret_cast<const float4*>(hr + I + c);
-        const float4 u1 = *reinterpret_cast<const float4*>(hr + I + c + 4);
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+        swiglu8(h + (size_t)r * 2 * I, I, c, v);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;

@@ -121,6 +121,13 @@ bool forward_fused_applies(int M, int k, int E, int K, int N, int chunk_rows);
 hipError_t launch_gemm_fp8_fused(const uint16_t* x, const int32_t* ids, int M, int k, int E,
                                  int K, const uint8_t* w, const float* w_scales, int N,
                                  float* rows_out, hipStream_t s);
+// The same GEMM as the FP8 MLP's down projection: the A rows are silu(g) * u of the fp32
+// gate+up rows h [M*k][2K] at route ids, requantised per 128 columns in the tile build (as
+// moe_swiglu_quant would); those codes [M*k][K] and scales [K/128][M*k] also go to a_q / a_s
+// when a_q is set.  rows_out [M*k][N] at route ids.
+hipError_t launch_gemm_fp8_fused_act(const float* h, const int32_t* ids, int M, int k, int E,
+                                     int K, const uint8_t* w, const float* w_scales, int N,
+                                     float* rows_out, uint8_t* a_q, float* a_s, hipStream_t s);
 // The same GEMM with the route inside (moe_route folded in): writes ids and weights, hands
 // the routes over through tagged words handoff [M*k] (untagged at launch; cleared by the
 // combine) and sets *status to 1 if a workgroup's wait gave up.  Applies where

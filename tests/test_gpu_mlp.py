@@ -143,14 +143,16 @@ def ws_part(ws, d, which, dtype, n):
 
 
 @pytest.mark.parametrize("M,E,k,H,I,chunk,kernels", [
-    (8, 16, 2, 256, 256, 0, 7),       # the correctness-sized layer; general GEMM for both
+    (8, 16, 2, 256, 256, 0, 3),       # the correctness-sized layer (both GEMMs at K = 256)
+    (8, 16, 2, 256, 256, 64, 7),      # the same with 64-row chunks: general GEMM for both
     (37, 5, 3, 384, 384, 64, 7),      # ragged segments, 64-row chunks
-    (64, 8, 2, 2048, 512, 16, 4),     # small batch: gate+up from the routed ids with the
-                                      # route inside, layout and activations in one launch,
-                                      # down GEMM gathering its rows by sorted route id
+    (64, 8, 2, 2048, 512, 16, 3),     # small batch: gate+up from the routed ids with the
+                                      # route inside, down GEMM from the same ids forming and
+                                      # requantising the activations of its rows itself
     (64, 8, 2, 2048, 512, 128, 7),    # LDS-tiled GEMM for both projections
-    (64, 8, 2, 1024, 512, 16, 4),     # small batch at hidden width 1024
-    (40, 16, 3, 512, 1024, 0, 4),     # ... and 512, expert width 1024
+    (64, 8, 2, 1024, 512, 16, 3),     # small batch at hidden width 1024
+    (40, 16, 3, 512, 1024, 0, 3),     # ... and 512, expert width 1024
+    (24, 12, 2, 2048, 256, 0, 3),     # expert width 256 (the down GEMM at K = 256)
 ])
 def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
     assert moe.mlp_forward_kernels(M, E, k, H, I, chunk) == kernels
@@ -163,8 +165,9 @@ def test_mlp_forward_matches_oracle(M, E, k, H, I, chunk, kernels):
     ids, _ = orc.route(d["logits"], k, CAP)
     counts, offsets = orc.layout(ids, E)
     np.testing.assert_array_equal(ws_part(ws, d, 0, np.int32, M * k).reshape(M, k), ids)
-    np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, E), counts)
-    np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), offsets)
+    if kernels == 7:                            # (the small-batch path builds no layout)
+        np.testing.assert_array_equal(ws_part(ws, d, 2, np.int32, E), counts)
+        np.testing.assert_array_equal(ws_part(ws, d, 3, np.int32, E + 1), offsets)
 
 
 def random_mlp_shapes(n=10, seed=2028):
@@ -232,7 +235,7 @@ def test_mlp_forward_full_size():
     d = synth.mlp_inputs(**{kk: v for kk, v in
                             synth.MLP_WORKLOADS["mlp_fp8_M128_E256_k8_H2048_I512"].items()})
     M, E, k, H, I = d["M"], d["E"], d["k"], d["H"], d["I"]
-    assert moe.mlp_forward_kernels(M, E, k, H, I) == 4
+    assert moe.mlp_forward_kernels(M, E, k, H, I) == 3
     outs, ws = gpu_mlp(d, reps=2)
     np.testing.assert_array_equal(outs[1], outs[0])
     toks = np.arange(M, dtype=np.int32)
