@@ -79,17 +79,14 @@ struct TileLds {
 // for lane (j, g), the 16 bytes at [kb*128 + half*64 + g*16] of routed row j, so a
 // wave-wide 16-byte LDS-direct load fills it (lane l lands at base + 16*l) and an MFMA
 // operand read is 1 KiB contiguous.  Rows past rc repeat row rb (their output column is never
-// stored).  The KB*16 scales ([k-block][row]) follow, one dword per lane.  GA: sorted row s is
-// row a_rows[s] of a and of the scales (the operand gathered on load).
-template <int KB, bool GA>
+// stored).  The KB*16 scales ([k-block][row]) follow, one dword per lane.
+template <int KB>
 __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ a,
                                          const float* __restrict__ a_scales, int rows, int rb,
-                                         int rc, uint4* frag, float* sa, int lane,
-                                         const int32_t* __restrict__ a_rows) {
+                                         int rc, uint4* frag, float* sa, int lane) {
     constexpr int K = KB * 128;
     const int j = lane & 15, g = lane >> 4;
-    int row = rb + (j < rc ? j : 0);
-    if (GA) row = a_rows[row];
+    const int row = rb + (j < rc ? j : 0);
     const uint8_t* src = a + (size_t)row * K + g * 16;
 #pragma unroll 2
     for (int f = 0; f < KB * 2; ++f)
@@ -99,8 +96,7 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ a,
     for (int i = 0; i < KB / 4; ++i) {
         const int t = i * 64 + lane;
         const int kb = t >> 4, r = t & 15;
-        int srow = rb + (r < rc ? r : 0);
-        if (GA) srow = a_rows[srow];
+        const int srow = rb + (r < rc ? r : 0);
         __builtin_amdgcn_global_load_lds(a_scales + (size_t)kb * rows + srow,
                                          (lds_void*)(sa + i * 64), 4, 0, 0);
     }
@@ -108,13 +104,13 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ a,
 
 
 // NT: weights are read with the non-temporal hint (streamed once, kept out of the caches).
-template <int KB, int EPI, bool NT, bool GA>
+template <int KB, int EPI, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_range_kernel(const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
                            const uint8_t* w, const float* __restrict__ w_scales,
                            const int4* __restrict__ tasks, const int32_t* __restrict__ ntasks,
                            const int32_t* __restrict__ sorted_ids, void* __restrict__ out,
-                           int rows, int N, const int32_t* __restrict__ a_rows) {
+                           int rows, int N) {
     constexpr int K = KB * 128;
     constexpr int kRing = KB < kRingMax ? KB : kRingMax;
     constexpr int P = KB / kRing;               // passes of the ring per subtask
@@ -191,7 +187,7 @@ void gemm_fp8_range_kernel(const uint8_t* __restrict__ a, const float* __restric
         t_end = last < ntile ? wb + nth_set_bit(starts, last) : wb + wn;
         for (int s = 0; s < last - first; ++s) {
             const TaskD d = load_task(tasks, wb + nth_set_bit(starts, first + s));
-            tile_dma<KB, GA>(a, a_scales, rows, d.rb, d.rc, L.frag[s], L.sa[s], lane, a_rows);
+            tile_dma<KB>(a, a_scales, rows, d.rb, d.rc, L.frag[s], L.sa[s], lane);
         }
         if (lane == 0) {
             s_starts = starts;
@@ -326,41 +322,29 @@ void gemm_fp8_range_kernel(const uint8_t* __restrict__ a, const float* __restric
     }
 }
 
-template <int KB, bool NT, bool GA>
-hipError_t launch_kr(const uint8_t* a, const float* a_scales, int rows, const uint8_t* w,
-                     const float* w_scales, int N, const moe_task* tasks,
-                     const int32_t* ntasks, int epilogue, const int32_t* sorted, void* out,
-                     int grid, hipStream_t s, const int32_t* a_rows) {
-    const int4* t = reinterpret_cast<const int4*>(tasks);
-    switch (epilogue) {
-        case MOE_EPI_STORE_BF16:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_BF16, NT, GA>),
-                               dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
-                               ntasks, sorted, out, rows, N, a_rows);
-            break;
-        case MOE_EPI_ROUTE_F32:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_ROUTE_F32, NT, GA>),
-                               dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
-                               ntasks, sorted, out, rows, N, a_rows);
-            break;
-        default:
-            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_F32, NT, GA>),
-                               dim3(grid), dim3(kThreads), 0, s, a, a_scales, w, w_scales, t,
-                               ntasks, sorted, out, rows, N, a_rows);
-    }
-    return hipGetLastError();
-}
-
 template <int KB, bool NT>
 hipError_t launch_kb(const uint8_t* a, const float* a_scales, int rows, const uint8_t* w,
                      const float* w_scales, int N, const moe_task* tasks,
                      const int32_t* ntasks, int epilogue, const int32_t* sorted, void* out,
-                     int grid, hipStream_t s, const int32_t* a_rows) {
-    if (a_rows)
-        return launch_kr<KB, NT, true>(a, a_scales, rows, w, w_scales, N, tasks, ntasks,
-                                       epilogue, sorted, out, grid, s, a_rows);
-    return launch_kr<KB, NT, false>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
-                                    sorted, out, grid, s, a_rows);
+                     int grid, hipStream_t s) {
+    const int4* t = reinterpret_cast<const int4*>(tasks);
+    switch (epilogue) {
+        case MOE_EPI_STORE_BF16:
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_BF16, NT>), dim3(grid),
+                               dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted,
+                               out, rows, N);
+            break;
+        case MOE_EPI_ROUTE_F32:
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_ROUTE_F32, NT>), dim3(grid),
+                               dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted,
+                               out, rows, N);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_fp8_range_kernel<KB, MOE_EPI_STORE_F32, NT>), dim3(grid),
+                               dim3(kThreads), 0, s, a, a_scales, w, w_scales, t, ntasks, sorted,
+                               out, rows, N);
+    }
+    return hipGetLastError();
 }
 
 #ifndef MOE_RANGE_NT
@@ -378,19 +362,19 @@ hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int ro
                                  const uint8_t* w, const float* w_scales, int N,
                                  const moe_task* tasks, const int32_t* ntasks, int max_tasks,
                                  int epilogue, const int32_t* sorted, void* out,
-                                 hipStream_t s, const int32_t* a_rows) {
+                                 hipStream_t s) {
     int grid = device_info().cu_count;          // one 8-wave workgroup per CU
     if (grid > max_tasks) grid = max_tasks;
     if (grid <= 0) return hipSuccess;
     constexpr bool nt = MOE_RANGE_NT != 0;
     if (K == 512)
         return launch_kb<4, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
-                                sorted, out, grid, s, a_rows);
+                                sorted, out, grid, s);
     if (K == 1024)
         return launch_kb<8, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
-                                sorted, out, grid, s, a_rows);
+                                sorted, out, grid, s);
     return launch_kb<16, nt>(a, a_scales, rows, w, w_scales, N, tasks, ntasks, epilogue,
-                             sorted, out, grid, s, a_rows);
+                             sorted, out, grid, s);
 }
 
 }  // namespace moe

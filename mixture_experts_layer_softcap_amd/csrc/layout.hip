@@ -221,25 +221,6 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(
                 sorted_route_ids, route_slots, n_blocks2, tasks2, ntasks2, queue2);
 }
 
-// The FP8 MLP's layout (the down projection's task list and the sorted route ids) and its
-// activation step in one launch: they are independent, and the down GEMM is the first kernel
-// that needs both.  Workgroup 0 builds the layout; every other workgroup runs 16 activation
-// pieces (swiglu_quant_piece), one per wave.
-__global__ __launch_bounds__(kThreads) void layout_swiglu_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int n_blocks, int chunk,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ cursors,
-    moe_task* __restrict__ tasks, int32_t* __restrict__ ntasks, uint32_t* __restrict__ queue,
-    int32_t* __restrict__ sorted_route_ids, const float* __restrict__ h, int I,
-    uint8_t* __restrict__ a_q, float* __restrict__ a_scales) {
-    if (blockIdx.x == 0) {
-        layout_body(ids, R, E, n_blocks, chunk, counts, offsets, cursors, tasks, ntasks, queue,
-                    sorted_route_ids, nullptr, 0, nullptr, nullptr, nullptr);
-        return;
-    }
-    const long long item = (long long)(blockIdx.x - 1) * kWaves + (threadIdx.x >> 6);
-    swiglu_quant_piece(h, R, I, a_q, a_scales, item, threadIdx.x & 63);
-}
-
 // Per-expert counts and exclusive offsets alone (the layout kernel without the task list).
 __global__ __launch_bounds__(kThreads) void counts_kernel(const int32_t* __restrict__ ids, int R,
                                                           int E, int32_t* __restrict__ counts,
@@ -404,20 +385,6 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
     hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kThreads), 0, s, ids, M * k, E, n_blocks,
                        chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
                        sorted_route_ids, route_slots, 0, nullptr, nullptr, nullptr);
-    return hipGetLastError();
-}
-
-hipError_t launch_layout_swiglu(const int32_t* ids, int M, int k, int E, int n_blocks,
-                                int chunk_rows, int32_t* counts, int32_t* offsets,
-                                int32_t* cursors, moe_task* tasks, int32_t* ntasks,
-                                uint32_t* queue, int32_t* sorted_route_ids, const float* h,
-                                int I, uint8_t* a_q, float* a_scales, hipStream_t s) {
-    const int R = M * k;
-    const long long pieces = (long long)R * ((I + 511) / 512);
-    const unsigned grid = (unsigned)(1 + (pieces + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(layout_swiglu_kernel, dim3(grid), dim3(kThreads), 0, s, ids, R, E,
-                       n_blocks, chunk_rows, counts, offsets, cursors, tasks, ntasks, queue,
-                       sorted_route_ids, h, I, a_q, a_scales);
     return hipGetLastError();
 }
 

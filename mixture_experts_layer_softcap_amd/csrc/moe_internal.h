@@ -47,13 +47,6 @@ hipError_t launch_layout(const int32_t* ids, int M, int k, int E, int n_blocks, 
                          int32_t* sorted_route_ids, int32_t* route_slots, hipStream_t s);
 
 // one layout pass writing two task lists over the same chunks (n_blocks and n_blocks2 panels)
-// The FP8 MLP's layout (sorted route ids, one task list) and its activation step
-// (moe_swiglu_quant on h [M*k][2I]) in one launch.
-hipError_t launch_layout_swiglu(const int32_t* ids, int M, int k, int E, int n_blocks,
-                                int chunk_rows, int32_t* counts, int32_t* offsets,
-                                int32_t* cursors, moe_task* tasks, int32_t* ntasks,
-                                uint32_t* queue, int32_t* sorted_route_ids, const float* h,
-                                int I, uint8_t* a_q, float* a_scales, hipStream_t s);
 hipError_t launch_layout2(const int32_t* ids, int M, int k, int E, int chunk_rows,
                           int32_t* counts, int32_t* offsets, int32_t* cursors, int n_blocks,
                           moe_task* tasks, int32_t* ntasks, uint32_t* queue, int n_blocks2,
@@ -79,12 +72,10 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scales, int rows, in
 
 // contiguous-range form for tasks of at most 16 routed rows and K = 2048
 bool gemm_fp8_range_applies(int K, int chunk_rows);
-// (a_rows != nullptr: sorted row s of the operand is row a_rows[s] of a and its scales)
 hipError_t launch_gemm_fp8_range(const uint8_t* a, const float* a_scales, int rows, int K,
                                  const uint8_t* w, const float* w_scales, int N,
                                  const moe_task* tasks, const int32_t* ntasks, int max_tasks,
-                                 int epilogue, const int32_t* sorted, void* out,
-                                 hipStream_t s, const int32_t* a_rows = nullptr);
+                                 int epilogue, const int32_t* sorted, void* out, hipStream_t s);
 
 // tiled form for chunks of 65..256 routed rows (both operands staged in LDS)
 bool gemm_fp8_tile_applies(int K, int chunk_rows);
