@@ -482,9 +482,9 @@ def bench_mlp(args, moe, synth, torch, np):
     lbytes = nonempty * (N1 * H + (N1 // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4) \
         + M * E * 4 + M * H * 2 + M * H * 2
     flops = 2.0 * R * (N1 * H + H * I)
-    gemm_kernel = (f"gemm_fp8_fused_kernel<{H // 128}, true, true> (the route inside the "
+    gemm_kernel = (f"gemm_fp8_fused_kernel<{H // 128}, true, true, false> (the route inside the "
                    "gate+up grouped FP8 GEMM from routed ids, rows at route ids)" if nkern == 3 else
-                   f"gemm_fp8_fused_kernel<{H // 128}, true, false> (gate+up grouped FP8 GEMM "
+                   f"gemm_fp8_fused_kernel<{H // 128}, true, false, false> (gate+up grouped FP8 GEMM "
                    "from routed ids, rows at route ids)" if fused else
                    "gemm_fp8_range_kernel (gate+up grouped FP8 GEMM, STORE_F32)"
                    if H == 2048 and chunk <= 16 else
@@ -724,10 +724,10 @@ def main():
         gemm_kernel = ("gemm_fp8_tile_kernel (grouped FP8 GEMM, LDS-staged tiles gathered from "
                        "token-major rows, ROUTE_F32)")
     elif nkern == 2:
-        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, true> (the route inside the "
+        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, true, false> (the route inside the "
                        "grouped FP8 GEMM from routed ids, rows at route ids)")
     elif fused:
-        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, false> (grouped FP8 GEMM from "
+        gemm_kernel = (f"gemm_fp8_fused_kernel<{K // 128}, true, false, false> (grouped FP8 GEMM from "
                        "routed ids, rows at route ids)")
     elif K in (512, 1024, 2048) and chunk <= 16:
         gemm_kernel = "gemm_fp8_range_kernel (grouped FP8 GEMM, ROUTE_F32)"
