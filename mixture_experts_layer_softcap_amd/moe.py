@@ -209,7 +209,8 @@ def grouped_gemm_gather(x_q, x_scales, k: int, w_q, w_scales, tasks, ntasks, chu
 
 def forward_kernels(M: int, E: int, k: int, K: int, N: int, chunk_rows: int = 0,
                     flags: int = 0) -> int:
-    """Kernels moe_forward_ex launches for these arguments (3 small batch, 5 otherwise)."""
+    """Kernels moe_forward_ex launches for these arguments: 2 or 3 at small batches (route
+    inside the GEMM or as a kernel of its own), 4 with LDS-tiled chunks, 5 staged."""
     n = lib().moe_forward_kernels(M, E, k, K, N, chunk_rows, flags)
     if n < 0:
         raise MoeError("moe_forward_kernels", n)

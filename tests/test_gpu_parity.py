@@ -1061,6 +1061,10 @@ def test_forward_fused_route_only_where_it_applies():
     assert moe.forward_kernels(8, 16, 2, 384, 256, 0, 0) == 5
     assert moe.forward_kernels(8, 16, 2, 4096, 256, 0, 0) == 5
     assert moe.forward_kernels(1024, 256, 8, 2048, 512, 0, 0) == 4
+    # the edge of the small-batch path: 2048 routed rows stay on it; 2056 (9 per expert,
+    # 16-row chunks) take the staged form
+    assert moe.forward_kernels(256, 256, 8, 2048, 512, 0, 0) == 2
+    assert moe.forward_kernels(257, 256, 8, 2048, 512, 0, 0) == 5
     assert moe.forward_kernels(128, 256, 8, 2048, 512, 0, moe.MOE_FWD_STAGED) == 5
 
 
